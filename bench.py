@@ -1,0 +1,225 @@
+"""Decode-step throughput of the sparse-decode hot path on one MI355X.
+
+Workload: the Llama-3-8B-shaped one-layer decode step at 32K context (batch 1,
+32 query / 8 KV heads, head_dim 128, d_imp 32, bf16 caches, budget 3277,
+radius 0, selection recomputed every step).  One step = tb_decode_step:
+append + project the new key, score every cached token, top-B select, and
+attend over the selected rows.  Inputs are seeded synthetic data already
+resident in HBM.  The caches are replicated R times at distinct addresses and
+the steps rotate over the replicas, so the 256 MB last-level cache cannot
+serve one step's reads from the previous steps.
+
+Prints one JSON line.  Extra legs:
+  roofline      the attention kernel (the step's largest HBM consumer), timed
+                with HIP events on its stream over K launches, against 8 TB/s;
+  cpu_baseline  the fp64 C oracle's decode step on the host (1 thread), on a
+                bounded number of steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from query_aware_kv_amd import synth  # noqa: E402
+from query_aware_kv_amd import tokenbutler as tbl  # noqa: E402
+from query_aware_kv_amd.workloads import LLAMA_32K  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "sparse decode steps/sec at 32K ctx (Llama-3-8B shape); achieved HBM GB/s vs peak"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def unique_rows(sel, cnt, w, ctx: int) -> tuple[int, int]:
+    """(unique K/V rows over the KV groups, logical rows over the query heads)
+    of one sequence, counted from the library's own index output; the always
+    kept appended token is included."""
+    s = sel[0].cpu().numpy()
+    c = cnt[0].cpu().numpy()
+    uniq = 0
+    logical = 0
+    G = w.n_q_heads // w.n_kv_heads
+    for g in range(w.n_kv_heads):
+        rows = {ctx - 1}
+        for h in range(g * G, (g + 1) * G):
+            i = h * w.n_imp_heads // w.n_q_heads
+            lst = set(s[i, :c[i]].tolist())
+            lst.add(ctx - 1)
+            logical += len(lst)
+            rows |= lst
+        uniq += len(rows)
+    return uniq, logical
+
+
+def cpu_baseline(w, pre, inp, seconds: float, max_steps: int) -> dict:
+    import oracle as orc
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
+    K = f64(pre.K[0])
+    Kp = np.zeros((w.n_kv_heads, w.ctx_cap, w.d_imp))
+    Kp[:, :w.ctx0] = orc.project(K[:, :w.ctx0], f64(pre.W), orc.BF16)  # set-up, not timed
+    st = orc.SequenceState(K, f64(pre.V[0]), Kp, w.n_imp_heads, w.budget, w.radius)
+    args = (f64(pre.W), f64(inp.q[0]), f64(inp.q_imp[0]))
+    kn, vn = f64(inp.k_new[0]), f64(inp.v_new[0])
+    n = 0
+    t0 = time.perf_counter()
+    while n < max_steps:
+        orc.decode_step(st, *args, w.ctx, orc.BF16, True, w.softmax_scale, k_new=kn, v_new=vn)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps of the 32K-context workload (append+project, score, "
+                      f"top-B, attend; fp64 C oracle, single thread, {dt:.1f} s)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (for HBM counter scaling)")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+              "sharding is described in the design notes but not built", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+
+    w = LLAMA_32K
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"bench: generating {w.name}")
+    pre = synth.prefill(w)
+    inp = synth.step_inputs(w, 0, pre)
+    shape = tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
+                           w.d_imp, w.ctx_cap, synth.torch_dtype(w))
+    params = tbl.make_params(w.budget, w.radius)
+    cap_s = tbl.selection_capacity(shape, params)
+
+    K0, V0, W = pre.K.to(dev), pre.V.to(dev), pre.W.to(dev)
+    Kp0 = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=K0.dtype, device=dev)
+    tbl.project_keys(shape, K0, W, torch.zeros(w.batch, dtype=torch.int32, device=dev), w.ctx0,
+                     Kp0)
+    reps = []
+    for r in range(a.replicas):
+        reps.append(dict(
+            K=K0.clone(), V=V0.clone(), Kp=Kp0.clone(),
+            sel=torch.zeros((w.batch, w.n_imp_heads, cap_s), dtype=torch.int32, device=dev),
+            cnt=torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev),
+            keep=torch.zeros(w.batch, dtype=torch.int32, device=dev)))
+    del K0, V0, Kp0
+    ws = tbl.alloc_workspace(shape, params, dev)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
+    q, qi = inp.q.to(dev), inp.q_imp.to(dev)
+    kn, vn = inp.k_new.to(dev), inp.v_new.to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device=dev)
+    step_args = [tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=True, w=W,
+                               k_cache=r["K"], v_cache=r["V"], kp_cache=r["Kp"], ctx_len=ctx,
+                               softmax_scale=w.softmax_scale, sel_idx=r["sel"],
+                               sel_count=r["cnt"], keep_from=r["keep"], out=out)
+                 for r in reps]
+    torch.cuda.synchronize()
+
+    R = len(reps)
+    log(f"bench: warmup {a.warmup}, timed {a.steps} fused steps over {R} replicas")
+    for s in range(a.warmup):
+        tbl.decode_step(shape, params, step_args[s % R], ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(a.steps):
+        tbl.decode_step(shape, params, step_args[s % R], ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / a.steps
+    log(f"bench: {ms_step * 1e3:.2f} us/step")
+
+    # dominant kernel: the gathered attention, launched alone on the same stream
+    for s in range(a.warmup):
+        r = reps[s % R]
+        tbl.sparse_attn(shape, q, r["K"], r["V"], r["sel"], cap_s, r["cnt"], r["keep"], ctx,
+                        w.softmax_scale, out, ws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(a.steps):
+        r = reps[s % R]
+        tbl.sparse_attn(shape, q, r["K"], r["V"], r["sel"], cap_s, r["cnt"], r["keep"], ctx,
+                        w.softmax_scale, out, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_attn = e0.elapsed_time(e1) / a.steps
+
+    uniq, logical = unique_rows(reps[0]["sel"], reps[0]["cnt"], w, w.ctx)
+    row_bytes = w.head_dim * w.elt_bytes
+    gather_bytes = uniq * 2 * row_bytes
+    kp_bytes = w.ctx * w.n_kv_heads * w.d_imp * w.elt_bytes
+    step_bytes = kp_bytes + gather_bytes
+    attn_gbs = gather_bytes / (ms_attn * 1e-3) / 1e9
+    step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    log(f"bench: attention {ms_attn * 1e3:.2f} us, {attn_gbs:.0f} GB/s; step {step_gbs:.0f} GB/s "
+        f"({uniq} unique rows, {logical} logical)")
+
+    if a.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        cpu = cpu_baseline(w, pre, inp, a.cpu_seconds, 200)
+
+    line = {
+        "metric": METRIC,
+        "value": 1e3 / ms_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/queries, 1% planted heavy tokens; bf16 caches)",
+        "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "imp_heads": w.n_imp_heads, "head_dim": w.head_dim, "d_imp": w.d_imp,
+                   "budget": w.budget, "radius": w.radius, "interval": w.interval,
+                   "storage": w.dtype, "replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "attn_kernel (tb_sparse_attn)",
+                     "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "algorithmic_bytes": gather_bytes, "us_per_launch": ms_attn * 1e3},
+        "step_hbm": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
+                     "frac": step_gbs / PEAK_HBM_GBS, "unique_rows": uniq,
+                     "logical_rows": logical},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

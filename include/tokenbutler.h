@@ -1,0 +1,220 @@
+/*
+ * tokenbutler.h -- C ABI of libtokenbutler.so, the MI355X (gfx950) sparse-decode
+ * hot path of TokenButler ("TokenButler: Token Importance is Predictable").
+ *
+ * At each decode step a low-dimensional importance query per head is scored
+ * against a learned low-dimensional projection of the cached keys; each head
+ * keeps its top-B tokens, optionally widened by neighbor fetching and reused
+ * across a prediction interval; exact softmax attention then runs over the
+ * gathered K/V rows only while the full cache stays resident.
+ *
+ * Citations name the page and section of the method description:
+ *   [ABS]  TokenButler abstract, 2026 version (author page, searcharxiv.com)
+ *   [ARCH] gist.science technical summary, Methodology > Core Architecture
+ *   [INF]  gist.science technical summary, Inference Strategy > Optimizations
+ *   [SIG]  gist.science technical summary, Significance
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device, except
+ *   the tb_shape / tb_select_params / tb_step_args structs themselves, which
+ *   are read on the host during the call.  The caller owns every buffer; the
+ *   library never allocates device memory, frees, or keeps a pointer after a
+ *   call returns.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *   the call returns without waiting for it.  Calls on one stream run in
+ *   order; calls that share a workspace must not overlap.
+ * - Element dtype: every K/V/Kp/W/q/q_imp/out tensor has the dtype of
+ *   tb_shape.dtype (TB_F32 or TB_BF16).  Scores are fp32.  Index tensors are
+ *   int32.
+ * - Layouts (row-major, innermost last):
+ *     K, V cache   [batch][n_kv_heads][ctx_cap][head_dim]
+ *     Kp cache     [batch][n_kv_heads][ctx_cap][d_imp]      (projected keys)
+ *     W            [head_dim][d_imp]  one matrix shared by all KV heads
+ *     q            [batch][n_q_heads][head_dim]
+ *     q_imp        [batch][n_imp_heads][d_imp]
+ *     scores       [batch][n_imp_heads][ctx_cap]
+ *     sel_idx      [batch][n_imp_heads][sel_stride]  ascending positions
+ *     sel_count    [batch][n_imp_heads]
+ *     ctx_len, keep_from, pos0   [batch]
+ *     out          [batch][n_q_heads][head_dim]
+ * - Head maps: query head h reads KV head h*Hkv/Hq and importance head
+ *   h*Himp/Hq; importance head i scores KV head i*Hkv/Himp (integer division).
+ * - ctx_len[b] is the number of valid cache rows of sequence b; values are
+ *   clamped to [0, ctx_cap] on the device.
+ * - Arithmetic: projected keys are fp64 sums in ascending head_dim order,
+ *   rounded once (to nearest even) to the dtype; scores are fp64 dot products
+ *   in ascending d_imp order rounded once to fp32; attention accumulates in
+ *   fp32.  Inputs must be finite.
+ * - Return value: TB_OK, or a negative TB_E* code.  Every argument check runs
+ *   on the host before anything is enqueued, so an error return means nothing
+ *   was launched -- except TB_EHIP, which reports a failed launch.
+ * - Workspace: calls that take `ws` need at least tb_workspace_bytes() bytes
+ *   of device memory, 256-byte aligned, ZERO-FILLED before its first use.
+ *   Every call leaves it zero-filled where that matters, so one allocation
+ *   can be reused; after a TB_EHIP error zero-fill it again.
+ */
+#ifndef TOKENBUTLER_H
+#define TOKENBUTLER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TB_OK 0
+#define TB_EINVAL (-1)       /* null pointer, bad size or inconsistent heads */
+#define TB_EUNSUPPORTED (-2) /* dtype / head_dim / d_imp / group size / ctx_cap outside the built set */
+#define TB_EWORKSPACE (-3)   /* workspace smaller than tb_workspace_bytes() */
+#define TB_EHIP (-4)         /* a kernel launch failed */
+
+#define TB_F32 0
+#define TB_BF16 1
+
+typedef struct tb_shape {
+    int32_t batch;       /* sequences, >= 1 */
+    int32_t n_q_heads;   /* Hq, a multiple of n_imp_heads */
+    int32_t n_kv_heads;  /* Hkv; Hq/Hkv in {1,2,4,8} */
+    int32_t n_imp_heads; /* Himp, a multiple of Hkv; Himp/Hkv in {1,2,4,8} */
+    int32_t head_dim;    /* D in {64, 128} */
+    int32_t d_imp;       /* d in {16, 32} */
+    int32_t ctx_cap;     /* cache capacity in tokens, 1 .. 262144 */
+    int32_t dtype;       /* TB_F32 or TB_BF16 */
+} tb_shape;
+
+typedef struct tb_select_params {
+    int32_t budget;  /* B >= 1: tokens kept per importance head before widening */
+    int32_t radius;  /* r in [0, 1024]: neighbor-fetch radius */
+    int32_t n_sink;  /* reserved, must be 0 */
+    int32_t n_local; /* reserved, must be 0 */
+} tb_select_params;
+
+/* Library version (major*10000 + minor*100 + patch).  Host only. */
+int tb_version(void);
+
+/* Static description of a return code.  Host only. */
+const char *tb_strerror(int code);
+
+/* Bytes of workspace needed by tb_score / tb_select / tb_sparse_attn /
+ * tb_decode_step for this shape, or 0 if the shape or params are invalid.
+ * Host only. */
+size_t tb_workspace_bytes(const tb_shape *shape, const tb_select_params *params);
+
+/* Capacity of one head's selected-index list: min(ctx_cap, (2r+1)*B).  The
+ * sel_idx stride written by tb_select and tb_decode_step.  0 if invalid. */
+int32_t tb_selection_capacity(const tb_shape *shape, const tb_select_params *params);
+
+/*
+ * tb_project_keys -- append-time key projection into the projected-key cache.
+ * [ARCH]: the real cache keys are mapped into the low-dimensional importance
+ * space by one learned matrix per consumer layer; [INF]: this is done for a
+ * batch of new tokens at a time rather than token by token.
+ *
+ * For every sequence b, KV head g and j in [0, n_tokens) with
+ * t = pos0[b] + j in [0, ctx_cap):
+ *     kp_cache[b][g][t][:] = round( k_cache[b][g][t][:] . W )   (fp64 sum)
+ * Rows with t outside [0, ctx_cap) are skipped.  pos0 is a device array.
+ * n_tokens == 0 is a no-op.  Errors: TB_EINVAL (null pointer, n_tokens < 0),
+ * TB_EUNSUPPORTED.
+ */
+int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
+                    const int32_t *pos0, int32_t n_tokens, void *kp_cache, void *stream);
+
+/*
+ * tb_score -- importance scores.  [ARCH]: each predicted importance query is
+ * dotted with the projected keys of its KV head.
+ *
+ * scores[b][i][t] = fp32( sum_j q_imp[b][i][j] * kp_cache[b][g(i)][t][j] )
+ * for t < ctx_len[b]; entries t >= ctx_len[b] are left untouched.
+ * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ */
+int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
+             const int32_t *ctx_len, float *scores, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * tb_select -- per-head top-B under a fixed budget, then neighbor fetching.
+ * [ABS], [ARCH]: per-token selection of the highest-scoring tokens under a
+ * fixed budget; [INF]: each kept token is widened to its spatial neighbors.
+ *
+ * For each (b, i) with n = ctx_len[b]:
+ *   T = the first min(B, n) tokens of [0, n) ordered by (score descending,
+ *       position ascending); -0.0 and +0.0 compare equal;
+ *   S = union over t in T of [max(0, t-r), min(n-1, t+r)].
+ * sel_idx[b][i][0 .. |S|) receives S ascending (stride
+ * tb_selection_capacity()), sel_count[b][i] = |S|.  If topb_idx is not NULL
+ * it receives T ascending with stride B (its count is min(B, n)).
+ * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ */
+int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
+              const int32_t *ctx_len, int32_t *sel_idx, int32_t *sel_count, int32_t *topb_idx,
+              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * tb_sparse_attn -- exact softmax attention over the selected rows only.
+ * [ABS], [SIG]: the full cache stays resident and each step reads only the
+ * selected tokens.
+ *
+ * For query head h (KV head g, importance head i) of sequence b with
+ * n = ctx_len[b], the attended set is
+ *   A = { sel_idx[b][i][k] : k < sel_count[b][i], value in [0, n) }
+ *       united with [keep_from[b], n) when keep_from is not NULL,
+ * and out[b][h] = sum_{t in A} softmax_t(scale * q[b][h] . K[b][g][t]) V[b][g][t],
+ * accumulated in fp32 and rounded to the dtype.  An empty A gives a zero row.
+ * sel_idx lists must be ascending and duplicate-free; sel_count is clamped to
+ * sel_stride.  Rows shared by several query heads of one KV head are read
+ * once.  Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ */
+int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
+                   const void *v_cache, const int32_t *sel_idx, int32_t sel_stride,
+                   const int32_t *sel_count, const int32_t *keep_from, const int32_t *ctx_len,
+                   float softmax_scale, void *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Arguments of one fused decode step (all pointers device pointers). */
+typedef struct tb_step_args {
+    const void *q;        /* [b][Hq][D] */
+    const void *q_imp;    /* [b][Himp][d]; read on refresh steps only */
+    const void *k_new;    /* [b][Hkv][n_new][D]; NULL iff n_new == 0 */
+    const void *v_new;    /* [b][Hkv][n_new][D]; NULL iff n_new == 0 */
+    int32_t n_new;        /* tokens appended by this step, >= 0 */
+    int32_t refresh;      /* non-zero: recompute the selection this step */
+    const void *w;        /* [D][d] key-projection matrix */
+    void *k_cache;        /* [b][Hkv][ctx_cap][D] */
+    void *v_cache;        /* [b][Hkv][ctx_cap][D] */
+    void *kp_cache;       /* [b][Hkv][ctx_cap][d] */
+    const int32_t *ctx_len; /* [b]: context length AFTER the append */
+    float softmax_scale;
+    int32_t *sel_idx;     /* state [b][Himp][tb_selection_capacity()] */
+    int32_t *sel_count;   /* state [b][Himp] */
+    int32_t *keep_from;   /* state [b] */
+    void *out;            /* [b][Hq][D] */
+} tb_step_args;
+
+/*
+ * tb_decode_step -- one fused decode step of one consumer layer.
+ * [INF]: projected keys are extended as tokens arrive; the predictor runs
+ * only every P steps (the caller sets `refresh` when step % P == 0) and its
+ * selection, widened by neighbor fetching, is reused in between; [ABS],
+ * [SIG]: attention reads only the selected rows.
+ *
+ * 1. The n_new rows of k_new / v_new are written to positions
+ *    [ctx_len[b] - n_new, ctx_len[b]) of the caches and their keys projected
+ *    (as tb_project_keys).
+ * 2. If refresh: scores over [0, ctx_len[b]) (as tb_score), T and S (as
+ *    tb_select) are stored in sel_idx / sel_count, and
+ *    keep_from[b] = ctx_len[b] - n_new.
+ * 3. out = attention over S united with [keep_from[b], ctx_len[b]) (as
+ *    tb_sparse_attn), so tokens appended since the last refresh are always
+ *    attended.
+ * On a non-refresh step the state is read, not written.  ctx_len[b] - n_new
+ * must be >= 0.  Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ */
+int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
+                   const tb_step_args *args, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENBUTLER_H */

@@ -1,0 +1,239 @@
+// tb_api.hip -- the C ABI of libtokenbutler: argument checks on the host,
+// workspace layout, and the launch sequence of each entry point.
+#include <string.h>
+
+#include "tb_internal.h"
+
+using namespace tb;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool pow2_group(int a, int b) // a / b in {1, 2, 4, 8}
+{
+    if (b <= 0 || a % b != 0)
+        return false;
+    const int g = a / b;
+    return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int check_shape(const tb_shape *s)
+{
+    if (s == nullptr)
+        return TB_EINVAL;
+    if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->n_imp_heads <= 0 ||
+        s->head_dim <= 0 || s->d_imp <= 0 || s->ctx_cap <= 0)
+        return TB_EINVAL;
+    if (s->n_q_heads % s->n_kv_heads != 0 || s->n_imp_heads % s->n_kv_heads != 0 ||
+        s->n_q_heads % s->n_imp_heads != 0)
+        return TB_EINVAL;
+    if (s->dtype != TB_F32 && s->dtype != TB_BF16)
+        return TB_EUNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128)
+        return TB_EUNSUPPORTED;
+    if (s->d_imp != 16 && s->d_imp != 32)
+        return TB_EUNSUPPORTED;
+    if (!pow2_group(s->n_q_heads, s->n_kv_heads) || !pow2_group(s->n_imp_heads, s->n_kv_heads))
+        return TB_EUNSUPPORTED;
+    if (s->ctx_cap > kMaxCtxCap)
+        return TB_EUNSUPPORTED;
+    return TB_OK;
+}
+
+int check_params(const tb_select_params *p)
+{
+    if (p == nullptr)
+        return TB_EINVAL;
+    if (p->budget <= 0 || p->radius < 0 || p->radius > 1024 || p->n_sink < 0 || p->n_local < 0)
+        return TB_EINVAL;
+    if (p->n_sink != 0 || p->n_local != 0)
+        return TB_EUNSUPPORTED;
+    return TB_OK;
+}
+
+int32_t sel_capacity(const tb_shape &s, const tb_select_params &p)
+{
+    const long long widened = (2LL * p.radius + 1) * (long long)p.budget;
+    return (int32_t)(widened < s.ctx_cap ? widened : s.ctx_cap);
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? TB_OK : TB_EHIP; }
+
+struct Ws {
+    double *q64;
+    float *scores;
+    float *part;
+    uint32_t *counters;
+};
+
+Ws carve(void *ws, const WsLayout &L)
+{
+    char *base = (char *)ws;
+    return Ws{(double *)(base + L.qimp64), (float *)(base + L.scores), (float *)(base + L.part),
+              (uint32_t *)(base + L.counters)};
+}
+
+int check_ws(const tb_shape &s, void *ws, size_t ws_bytes, WsLayout *L)
+{
+    *L = ws_layout(s);
+    if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0)
+        return TB_EINVAL;
+    if (ws_bytes < L->total)
+        return TB_EWORKSPACE;
+    return TB_OK;
+}
+
+#define TB_TRY(x)                                                                                  \
+    do {                                                                                           \
+        const int rc_ = (x);                                                                       \
+        if (rc_ != TB_OK)                                                                          \
+            return rc_;                                                                            \
+    } while (0)
+
+} // namespace
+
+extern "C" {
+
+int tb_version(void) { return 10000; }
+
+const char *tb_strerror(int code)
+{
+    switch (code) {
+    case TB_OK: return "ok";
+    case TB_EINVAL: return "invalid argument (null pointer, bad size, misaligned pointer or inconsistent head counts)";
+    case TB_EUNSUPPORTED: return "unsupported dtype, head_dim, d_imp, group size, ctx_cap or reserved parameter";
+    case TB_EWORKSPACE: return "workspace smaller than tb_workspace_bytes()";
+    case TB_EHIP: return "HIP kernel launch failed";
+    }
+    return "unknown tokenbutler error code";
+}
+
+size_t tb_workspace_bytes(const tb_shape *shape, const tb_select_params *params)
+{
+    if (check_shape(shape) != TB_OK)
+        return 0;
+    if (params != nullptr && check_params(params) != TB_OK)
+        return 0;
+    return ws_layout(*shape).total;
+}
+
+int32_t tb_selection_capacity(const tb_shape *shape, const tb_select_params *params)
+{
+    if (check_shape(shape) != TB_OK || check_params(params) != TB_OK)
+        return 0;
+    return sel_capacity(*shape, *params);
+}
+
+int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
+                    const int32_t *pos0, int32_t n_tokens, void *kp_cache, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    if (k_cache == nullptr || w == nullptr || pos0 == nullptr || kp_cache == nullptr ||
+        n_tokens < 0)
+        return TB_EINVAL;
+    if (!aligned16(k_cache) || !aligned16(kp_cache))
+        return TB_EINVAL;
+    if (n_tokens == 0)
+        return TB_OK;
+    if ((long long)shape->batch * shape->n_kv_heads * n_tokens > 0x7fffffffLL)
+        return TB_EINVAL;
+    return hip_rc(launch_project(*shape, k_cache, w, pos0, n_tokens, kp_cache,
+                                 (hipStream_t)stream));
+}
+
+int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
+             const int32_t *ctx_len, float *scores, void *ws, size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    if (q_imp == nullptr || kp_cache == nullptr || ctx_len == nullptr || scores == nullptr)
+        return TB_EINVAL;
+    if (!aligned16(kp_cache))
+        return TB_EINVAL;
+    WsLayout L;
+    TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    Ws W = carve(ws, L);
+    hipStream_t st = (hipStream_t)stream;
+    TB_TRY(hip_rc(launch_qimp_f64(*shape, q_imp, W.q64, ctx_len, 0, nullptr, st)));
+    return hip_rc(launch_score(*shape, W.q64, kp_cache, ctx_len, scores, st));
+}
+
+int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
+              const int32_t *ctx_len, int32_t *sel_idx, int32_t *sel_count, int32_t *topb_idx,
+              void *ws, size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    TB_TRY(check_params(params));
+    if (scores == nullptr || ctx_len == nullptr || sel_idx == nullptr || sel_count == nullptr)
+        return TB_EINVAL;
+    WsLayout L;
+    TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
+                                sel_capacity(*shape, *params), sel_count, topb_idx,
+                                (hipStream_t)stream));
+}
+
+int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
+                   const void *v_cache, const int32_t *sel_idx, int32_t sel_stride,
+                   const int32_t *sel_count, const int32_t *keep_from, const int32_t *ctx_len,
+                   float softmax_scale, void *out, void *ws, size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || sel_idx == nullptr ||
+        sel_count == nullptr || ctx_len == nullptr || out == nullptr || sel_stride <= 0)
+        return TB_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return TB_EINVAL;
+    if (!(softmax_scale == softmax_scale))
+        return TB_EINVAL;
+    WsLayout L;
+    TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    Ws W = carve(ws, L);
+    return hip_rc(launch_attn(*shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count,
+                              keep_from, ctx_len, softmax_scale, out, W.part, W.counters,
+                              (hipStream_t)stream));
+}
+
+int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
+                   const tb_step_args *a, void *ws, size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    TB_TRY(check_params(params));
+    if (a == nullptr)
+        return TB_EINVAL;
+    if (a->q == nullptr || a->w == nullptr || a->k_cache == nullptr || a->v_cache == nullptr ||
+        a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_idx == nullptr ||
+        a->sel_count == nullptr || a->keep_from == nullptr || a->out == nullptr)
+        return TB_EINVAL;
+    if (a->n_new < 0 || (a->n_new > 0 && (a->k_new == nullptr || a->v_new == nullptr)))
+        return TB_EINVAL;
+    if (a->refresh && a->q_imp == nullptr)
+        return TB_EINVAL;
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
+        !aligned16(a->kp_cache))
+        return TB_EINVAL;
+    if (!(a->softmax_scale == a->softmax_scale))
+        return TB_EINVAL;
+    WsLayout L;
+    TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    Ws W = carve(ws, L);
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t stride = sel_capacity(*shape, *params);
+
+    if (a->n_new > 0)
+        TB_TRY(hip_rc(launch_append_project(*shape, a->k_new, a->v_new, a->n_new, a->w,
+                                            a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
+                                            st)));
+    if (a->refresh) {
+        TB_TRY(hip_rc(launch_qimp_f64(*shape, a->q_imp, W.q64, a->ctx_len, a->n_new,
+                                      a->keep_from, st)));
+        TB_TRY(hip_rc(launch_score(*shape, W.q64, a->kp_cache, a->ctx_len, W.scores, st)));
+        TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
+                                    a->sel_count, nullptr, st)));
+    }
+    return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
+                              a->sel_count, a->keep_from, a->ctx_len, a->softmax_scale, a->out,
+                              W.part, W.counters, st));
+}
+
+} // extern "C"

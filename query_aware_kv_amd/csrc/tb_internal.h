@@ -1,0 +1,136 @@
+// tb_internal.h -- shared device helpers and launcher declarations of
+// libtokenbutler (gfx950 only).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tokenbutler.h"
+
+namespace tb {
+
+// ---------------------------------------------------------------- dtypes
+// Storage element types: fp32 (`float`) and bf16 (raw bits in `uint16_t`).
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ double to_f64(float x) { return (double)x; }
+__device__ __forceinline__ double to_f64(bf16_t x) { return (double)to_f32(x); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (bf16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// fp64 -> bf16, correctly rounded (to nearest even) in one step.  Rounding
+// through fp32 first could round twice, so the 53-bit significand is cut
+// directly: 8 significant bits in the normal range, multiples of 2^-133 below
+// 2^-126.
+__device__ __forceinline__ bf16_t f64_to_bf16(double x)
+{
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    uint32_t sign = (uint32_t)(u >> 63) << 15;
+    int ex = (int)((u >> 52) & 0x7ff);
+    uint64_t man = u & 0xFFFFFFFFFFFFFull;
+    if (ex == 0x7ff)
+        return (bf16_t)(sign | 0x7f80u | (man ? 0x40u : 0u));
+    if (ex == 0)
+        return (bf16_t)sign; // fp64 zero / subnormal: far below bf16's range
+    int e = ex - 1023;
+    if (e > 127)
+        return (bf16_t)(sign | 0x7f80u);
+    int shift = e >= -126 ? 45 : -81 - e;
+    if (shift > 60)
+        return (bf16_t)sign;
+    uint64_t full = man | (1ull << 52);
+    uint64_t keep = full >> shift;
+    uint64_t rem = full & ((1ull << shift) - 1);
+    uint64_t half = 1ull << (shift - 1);
+    if (rem > half || (rem == half && (keep & 1)))
+        keep += 1;
+    if (e >= -126) {
+        if (keep == 256) {
+            keep = 128;
+            e += 1;
+            if (e > 127)
+                return (bf16_t)(sign | 0x7f80u);
+        }
+        return (bf16_t)(sign | ((uint32_t)(e + 127) << 7) | (uint32_t)(keep & 0x7f));
+    }
+    return (bf16_t)(sign | (uint32_t)keep); // keep == 128 encodes 2^-126
+}
+
+template <typename T> __device__ __forceinline__ T from_f64(double x);
+template <> __device__ __forceinline__ float from_f64<float>(double x) { return (float)x; }
+template <> __device__ __forceinline__ bf16_t from_f64<bf16_t>(double x) { return f64_to_bf16(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+__device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
+
+// ---------------------------------------------------------------- sizes
+constexpr int kAttnChunk = 512;     // positions per attention work-group
+constexpr int kMaxCtxCap = 262144;  // bounded by the selection kernel's LDS bitmaps
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout (offsets in bytes from the workspace base).
+struct WsLayout {
+    size_t qimp64;   // fp64 copy of q_imp [b][Himp][d]
+    size_t scores;   // fp32 scores [b][Himp][cap] (fused step only)
+    size_t part;     // attention partials [b][Hq][nchunk][D + 2] fp32
+    size_t counters; // attention arrival counters [b][Hkv] u32 (kept zero)
+    size_t total;
+};
+
+inline int attn_chunks(int cap) { return (cap + kAttnChunk - 1) / kAttnChunk; }
+
+inline WsLayout ws_layout(const tb_shape &s)
+{
+    WsLayout L;
+    size_t off = 0;
+    L.qimp64 = off;
+    off += align_up((size_t)s.batch * s.n_imp_heads * s.d_imp * sizeof(double));
+    L.scores = off;
+    off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(float));
+    L.part = off;
+    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * (s.head_dim + 2) *
+                    sizeof(float));
+    L.counters = off;
+    off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes are already validated.
+hipError_t launch_project(const tb_shape &s, const void *k_cache, const void *w,
+                          const int32_t *pos0, int n_tokens, void *kp_cache, hipStream_t st);
+hipError_t launch_append_project(const tb_shape &s, const void *k_new, const void *v_new,
+                                 int n_new, const void *w, void *k_cache, void *v_cache,
+                                 void *kp_cache, const int32_t *ctx_len, hipStream_t st);
+hipError_t launch_qimp_f64(const tb_shape &s, const void *q_imp, double *q64,
+                           const int32_t *ctx_len, int n_new, int32_t *keep_from,
+                           hipStream_t st);
+hipError_t launch_score(const tb_shape &s, const double *q64, const void *kp_cache,
+                        const int32_t *ctx_len, float *scores, hipStream_t st);
+hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
+                         const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
+                         int32_t *sel_count, int32_t *topb_idx, hipStream_t st);
+hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *sel_idx, int sel_stride,
+                       const int32_t *sel_count, const int32_t *keep_from,
+                       const int32_t *ctx_len, float softmax_scale, void *out, float *part,
+                       uint32_t *counters, hipStream_t st);
+
+} // namespace tb

@@ -1,0 +1,348 @@
+// tb_select.hip -- per-head top-B selection and neighbor fetching (gfx950).
+//
+// TokenButler abstract (2026) and gist.science technical summary,
+// Methodology > Core Architecture: per-token selection of the highest-scoring
+// tokens under a fixed budget B.  Inference Strategy > Optimizations: neighbor
+// fetching widens each kept token t to [t-r, t+r].
+//
+// One 1024-thread work-group per (sequence, importance head):
+//   1. Scores become order-preserving u32 keys (-0 folded onto +0).
+//   2. Radix select, 4 passes of 8 bits from the top: per-wave LDS histograms
+//      of the keys that match the prefix found so far, then a wave-wide
+//      suffix scan picks the digit holding the B-th largest key.  This yields
+//      the threshold key tau and how many of the keys equal to tau are kept
+//      (the lowest positions first).
+//   3. A ballot pass writes the kept set T as a bitmap in LDS; a block scan of
+//      per-word tie counts settles ties at tau by position.
+//   4. Dilation by r is word-wise shifts of the bitmap (clipped to [0, n)).
+//   5. A block scan of per-word popcounts compacts the bitmap into the
+//      ascending index list.
+// When every key fits in registers (n <= 64 per thread) the scores are read
+// from memory once; otherwise every pass streams them again.
+#include "tb_internal.h"
+
+namespace tb {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u)
+        u = 0u; // -0.0 ties with +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of popcount(words[w]) over w < nw into out[w]; returns
+// the total to every thread.  wsum: kSelWaves + 1 words of LDS scratch.
+__device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int nw,
+                                      uint32_t *wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (nw + kSelThreads - 1) / kSelThreads;
+    const int w0 = tid * per;
+    uint32_t local = 0;
+    for (int w = w0; w < w0 + per && w < nw; ++w)
+        local += __popc(words[w]);
+    // inclusive scan within the wave
+    uint32_t inc = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t v = __shfl_up(inc, off);
+        if (lane >= off)
+            inc += v;
+    }
+    if (lane == 63)
+        wsum[wave] = inc;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t v = lane < kSelWaves ? wsum[lane] : 0u;
+        uint32_t x = v;
+#pragma unroll
+        for (int off = 1; off < kSelWaves; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off)
+                x += y;
+        }
+        if (lane < kSelWaves)
+            wsum[lane] = x - v; // exclusive prefix of waves
+        if (lane == kSelWaves - 1)
+            wsum[kSelWaves] = x; // total
+    }
+    __syncthreads();
+    uint32_t run = wsum[wave] + inc - local;
+    for (int w = w0; w < w0 + per && w < nw; ++w) {
+        out[w] = run;
+        run += __popc(words[w]);
+    }
+    const uint32_t total = wsum[kSelWaves];
+    __syncthreads();
+    return total;
+}
+
+// Writes the positions of the set bits of words[0..nw) in ascending order.
+__device__ void compact_bits(const uint32_t *words, const uint32_t *offs, int nw, int32_t *dst)
+{
+    for (int w = threadIdx.x; w < nw; w += kSelThreads) {
+        uint32_t bits = words[w];
+        int pos = (int)offs[w];
+        while (bits) {
+            const int bi = __ffs(bits) - 1;
+            dst[pos++] = w * 32 + bi;
+            bits &= bits - 1u;
+        }
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
+    int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
+    int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx)
+{
+    extern __shared__ uint32_t lds[];
+    uint32_t *hist = lds;                      // [kSelWaves][256]
+    uint32_t *misc = hist + kSelWaves * 256;   // 64 words
+    uint32_t *Tb = misc + 64;                  // [nwc] kept set
+    uint32_t *Sb = Tb + nwc;                   // [nwc] widened set / tie bits
+    uint32_t *Xb = Sb + nwc;                   // [nwc] dilation ping-pong
+    uint32_t *scan = Xb + nwc;                 // [nwc] scan output
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.y, i = blockIdx.x;
+    const size_t rowid = (size_t)b * Himp + i;
+    const float *row = scores + rowid * cap;
+    const int n = clamp_len(ctx_len[b], cap);
+    int32_t *out_sel = sel_idx + rowid * sel_stride;
+    if (n == 0) {
+        if (tid == 0)
+            sel_count[rowid] = 0;
+        return;
+    }
+    const int nw = (n + 31) >> 5;
+    const int nk = (n + kSelThreads - 1) / kSelThreads;
+
+    // Keys of this thread: keys[k] belongs to position k * kSelThreads + tid.
+    constexpr int KR = KPT > 0 ? KPT : 1;
+    uint32_t keys[KR];
+    if constexpr (KPT > 0) {
+#pragma unroll
+        for (int k = 0; k < KR; ++k) {
+            const int t = k * kSelThreads + tid;
+            keys[k] = t < n ? score_key(row[t]) : 0u;
+        }
+    }
+
+    const bool take_all = B >= n;
+    uint32_t tau = 0u, need = 0u, cnt_eq = 0u;
+    if (!take_all) {
+        uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int e = tid; e < kSelWaves * 256; e += kSelThreads)
+                hist[e] = 0u;
+            __syncthreads();
+            uint32_t *h = hist + wave * 256;
+            if constexpr (KPT > 0) {
+#pragma unroll
+                for (int k = 0; k < KR; ++k) {
+                    const int t = k * kSelThreads + tid;
+                    const uint32_t key = keys[k];
+                    if (t < n && (key & pmask) == prefix)
+                        atomicAdd(&h[(key >> shift) & 255u], 1u);
+                }
+            } else {
+                for (int k = 0; k < nk; ++k) {
+                    const int t = k * kSelThreads + tid;
+                    if (t < n) {
+                        const uint32_t key = score_key(row[t]);
+                        if ((key & pmask) == prefix)
+                            atomicAdd(&h[(key >> shift) & 255u], 1u);
+                    }
+                }
+            }
+            __syncthreads();
+            if (tid < 256) {
+                uint32_t c = 0u;
+#pragma unroll
+                for (int w = 0; w < kSelWaves; ++w)
+                    c += hist[w * 256 + tid];
+                hist[tid] = c;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
+                const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+                const uint32_t sl = c0 + c1 + c2 + c3;
+                uint32_t suf = sl; // inclusive suffix sum over lanes
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t v = __shfl_down(suf, off);
+                    if (lane + off < 64)
+                        suf += v;
+                }
+                const unsigned long long m = __ballot(suf >= krem);
+                const int L = 63 - __clzll(m);
+                if (lane == L) {
+                    uint32_t above = suf - sl;
+                    uint32_t dg, cd;
+                    if (above + c3 >= krem) {
+                        dg = 4u * L + 3u;
+                        cd = c3;
+                    } else if (above + c3 + c2 >= krem) {
+                        above += c3;
+                        dg = 4u * L + 2u;
+                        cd = c2;
+                    } else if (above + c3 + c2 + c1 >= krem) {
+                        above += c3 + c2;
+                        dg = 4u * L + 1u;
+                        cd = c1;
+                    } else {
+                        above += c3 + c2 + c1;
+                        dg = 4u * L;
+                        cd = c0;
+                    }
+                    misc[0] = prefix | (dg << shift);
+                    misc[1] = krem - above;
+                    misc[2] = cd;
+                }
+            }
+            __syncthreads();
+            prefix = misc[0];
+            krem = misc[1];
+            cnt_eq = misc[2];
+            pmask |= 255u << shift;
+            __syncthreads();
+        }
+        tau = prefix;
+        need = krem; // keys equal to tau that are kept, lowest positions first
+    }
+    const bool partial_ties = !take_all && need < cnt_eq;
+
+    // ---- kept-set bitmap (and tie bitmap when ties are split) ----
+    auto emit = [&](int k, uint32_t key) {
+        const int t = k * kSelThreads + tid;
+        const bool valid = t < n;
+        const bool gt = valid && (take_all || key > tau || (!partial_ties && key == tau));
+        const bool eq = valid && partial_ties && key == tau;
+        const unsigned long long mg = __ballot(gt);
+        const unsigned long long me = __ballot(eq);
+        const int w0 = (k * kSelThreads + wave * 64) >> 5;
+        if (lane == 0 && w0 < nw) {
+            Tb[w0] = (uint32_t)mg;
+            Sb[w0] = (uint32_t)me;
+        }
+        if (lane == 0 && w0 + 1 < nw) {
+            Tb[w0 + 1] = (uint32_t)(mg >> 32);
+            Sb[w0 + 1] = (uint32_t)(me >> 32);
+        }
+    };
+    if constexpr (KPT > 0) {
+#pragma unroll
+        for (int k = 0; k < KR; ++k)
+            emit(k, keys[k]);
+    } else {
+        for (int k = 0; k < nk; ++k) {
+            const int t = k * kSelThreads + tid;
+            emit(k, t < n ? score_key(row[t]) : 0u);
+        }
+    }
+    __syncthreads();
+    if (partial_ties) {
+        block_popc_exscan(Sb, scan, nw, misc + 8);
+        for (int w = tid; w < nw; w += kSelThreads) {
+            uint32_t e = Sb[w];
+            const uint32_t pre = scan[w];
+            if (pre >= need) {
+                e = 0u;
+            } else if (pre + __popc(e) > need) {
+                uint32_t m = e;
+                for (uint32_t c = need - pre; c > 0u; --c)
+                    m &= m - 1u;
+                e ^= m; // the lowest (need - pre) tie bits
+            }
+            Tb[w] |= e;
+        }
+        __syncthreads();
+    }
+
+    // ---- optional pre-widening output ----
+    if (topb_idx != nullptr) {
+        block_popc_exscan(Tb, scan, nw, misc + 8);
+        compact_bits(Tb, scan, nw, topb_idx + rowid * (size_t)B);
+        __syncthreads();
+    }
+
+    // ---- neighbor fetching: dilate T by r within [0, n) ----
+    const uint32_t *fin = Tb;
+    if (r > 0) {
+        const uint32_t *src = Tb;
+        uint32_t *dst = Sb;
+        int left = r;
+        while (left > 0) {
+            const int step = left < 31 ? left : 31;
+            for (int w = tid; w < nw; w += kSelThreads) {
+                const uint32_t x = src[w];
+                const uint32_t prv = w > 0 ? src[w - 1] : 0u;
+                const uint32_t nxt = w + 1 < nw ? src[w + 1] : 0u;
+                uint32_t res = x;
+                for (int s2 = 1; s2 <= step; ++s2)
+                    res |= (x << s2) | (prv >> (32 - s2)) | (x >> s2) | (nxt << (32 - s2));
+                if (w == nw - 1 && (n & 31))
+                    res &= (1u << (n & 31)) - 1u;
+                dst[w] = res;
+            }
+            __syncthreads();
+            left -= step;
+            fin = dst;
+            src = dst;
+            dst = (dst == Sb) ? Xb : Sb;
+        }
+    }
+
+    // ---- compaction into the ascending list ----
+    const uint32_t total = block_popc_exscan(fin, scan, nw, misc + 8);
+    compact_bits(fin, scan, nw, out_sel);
+    if (tid == 0)
+        sel_count[rowid] = (int32_t)total;
+}
+
+template <int KPT>
+hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
+                    const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
+                    int32_t *sel_count, int32_t *topb_idx, hipStream_t st)
+{
+    const int nwc = (s.ctx_cap + 31) / 32 + 1;
+    const size_t lds = ((size_t)kSelWaves * 256 + 64 + 4 * (size_t)nwc) * sizeof(uint32_t);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<KPT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    dim3 grid(s.n_imp_heads, s.batch);
+    hipLaunchKernelGGL(select_kernel<KPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
+                       s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx, sel_stride,
+                       sel_count, topb_idx);
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
+                         const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
+                         int32_t *sel_count, int32_t *topb_idx, hipStream_t st)
+{
+    const int per = (s.ctx_cap + kSelThreads - 1) / kSelThreads;
+    if (per <= 1) return select_t<1>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 2) return select_t<2>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 4) return select_t<4>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 8) return select_t<8>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 16) return select_t<16>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 32) return select_t<32>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    return select_t<0>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+}
+
+} // namespace tb

@@ -1,0 +1,123 @@
+"""Shared set-up for the GPU parity tests: seeded inputs on the device through
+the library, and the same inputs in float64 for the oracle.
+
+Nothing here computes any part of the method: the GPU side calls the C ABI
+and the oracle side calls ``oracle``."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from query_aware_kv_amd import synth
+from query_aware_kv_amd import tokenbutler as tbl
+from query_aware_kv_amd.workloads import Workload
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    tbl.lib()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def odtype(w: Workload) -> int:
+    return orc.F32 if w.dtype == "f32" else orc.BF16
+
+
+@dataclass
+class DeviceCase:
+    w: Workload
+    pre: synth.Prefill
+    shape: tbl.Shape
+    params: tbl.SelectParams
+    cap_s: int
+    K: torch.Tensor
+    V: torch.Tensor
+    Kp: torch.Tensor
+    W: torch.Tensor
+    ws: torch.Tensor
+    sel: torch.Tensor
+    cnt: torch.Tensor
+    keep: torch.Tensor
+
+
+def shape_of(w: Workload) -> tbl.Shape:
+    return tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
+                          w.d_imp, w.ctx_cap, synth.torch_dtype(w))
+
+
+def device_case(w: Workload, layer: int = 0, pre: synth.Prefill | None = None) -> DeviceCase:
+    """Upload the prefill and project its keys with tb_project_keys."""
+    pre = pre if pre is not None else synth.prefill(w, layer)
+    dev = "cuda"
+    shape = shape_of(w)
+    params = tbl.make_params(w.budget, w.radius)
+    cap_s = tbl.selection_capacity(shape, params)
+    K = pre.K.to(dev)
+    V = pre.V.to(dev)
+    W = pre.W.to(dev)
+    Kp = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=K.dtype, device=dev)
+    pos0 = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    tbl.project_keys(shape, K, W, pos0, w.ctx0, Kp)
+    ws = tbl.alloc_workspace(shape, params, dev)
+    sel = torch.full((w.batch, w.n_imp_heads, cap_s), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev)
+    keep = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    return DeviceCase(w, pre, shape, params, cap_s, K, V, Kp, W, ws, sel, cnt, keep)
+
+
+def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Tensor):
+    """tb_decode_step for step s (one appended token per sequence)."""
+    w = dc.w
+    ctx = torch.full((w.batch,), w.ctx0 + s + 1, dtype=torch.int32, device="cuda")
+    q = inp.q.to("cuda")
+    qi = inp.q_imp.to("cuda") if inp.q_imp is not None else None
+    kn = inp.k_new.to("cuda")
+    vn = inp.v_new.to("cuda")
+    args = tbl.step_args(dc.shape, dc.params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=inp.refresh, w=dc.W,
+                         k_cache=dc.K, v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
+                         softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
+                         keep_from=dc.keep, out=out)
+    tbl.decode_step(dc.shape, dc.params, args, dc.ws)
+    torch.cuda.synchronize()
+    return ctx
+
+
+def oracle_state(w: Workload, pre: synth.Prefill, b: int) -> orc.SequenceState:
+    """Oracle caches of sequence b: the prefill rows and their projections."""
+    K = f64(pre.K[b])
+    V = f64(pre.V[b])
+    Kp = np.zeros((w.n_kv_heads, w.ctx_cap, w.d_imp))
+    Kp[:, :w.ctx0] = orc.project(K[:, :w.ctx0], f64(pre.W), odtype(w))
+    return orc.SequenceState(K, V, Kp, Himp=w.n_imp_heads, B=w.budget, r=w.radius)
+
+
+def oracle_step(w: Workload, st: orc.SequenceState, pre: synth.Prefill, inp: synth.StepInputs,
+                s: int, b: int) -> np.ndarray:
+    return orc.decode_step(st, f64(pre.W), f64(inp.q[b]),
+                           f64(inp.q_imp[b]) if inp.q_imp is not None else None,
+                           w.ctx0 + s + 1, odtype(w), inp.refresh, w.softmax_scale,
+                           k_new=f64(inp.k_new[b]), v_new=f64(inp.v_new[b]))
+
+
+def lists_of(sel: torch.Tensor, cnt: torch.Tensor, b: int) -> list:
+    s = sel[b].cpu().numpy()
+    c = cnt[b].cpu().numpy()
+    return [s[i, :c[i]].tolist() for i in range(s.shape[0])]
+
+
+def band_members(s32: np.ndarray, B: int, rel: float = 1e-6) -> np.ndarray:
+    """Tokens whose score lies within rel * |tau| of the B-th largest score."""
+    if B >= s32.size:
+        return np.zeros(0, dtype=np.int64)
+    tau = np.sort(s32.astype(np.float64))[::-1][B - 1]
+    return np.nonzero(np.abs(s32.astype(np.float64) - tau) <= rel * abs(tau))[0]

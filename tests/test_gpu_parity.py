@@ -1,0 +1,350 @@
+"""GPU parity: every stage of the HIP path, called through the C ABI, against
+the fp64 CPU oracle on the same seeded inputs.
+
+Bars: projected keys, scores and index sets bit-exact (both sides round the
+same fp64 sums once, so the selection keys agree bit for bit); attention
+outputs within max-abs 1e-4 (fp32) / 2e-2 (bf16)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from query_aware_kv_amd import synth
+from query_aware_kv_amd import tokenbutler as tbl
+from query_aware_kv_amd.workloads import (BATCHED_8K, INTERVAL_16K, LLAMA_32K, LONG_128K,
+                                          TINY_F32, Workload)
+from tests.gpu_cases import (TOL, band_members, device_case, f64, lists_of, need_gpu, odtype,
+                             oracle_state, oracle_step, shape_of, step_on_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _imp(w, h):
+    return h * w.n_imp_heads // w.n_q_heads
+
+
+def _kv(w, h):
+    return h * w.n_kv_heads // w.n_q_heads
+
+
+# --------------------------------------------------------------------------
+# stage by stage: projection -> scores -> selection -> attention
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [TINY_F32, LLAMA_32K], ids=lambda w: w.name)
+def test_stage_parity(w):
+    dc = device_case(w)
+    pre = dc.pre
+    b = 0
+    ctx = w.ctx
+    dt = odtype(w)
+    W64 = f64(pre.W)
+    # prefill projection: bit-exact
+    K64 = f64(pre.K[b])
+    Kp_ref = np.zeros((w.n_kv_heads, w.ctx_cap, w.d_imp))
+    Kp_ref[:, :w.ctx0] = orc.project(K64[:, :w.ctx0], W64, dt)
+    np.testing.assert_array_equal(f64(dc.Kp[b][:, :w.ctx0]), Kp_ref[:, :w.ctx0])
+    # append the step's token (a plain copy) and project that one row
+    dc.K[:, :, w.ctx0] = pre.k_next[:, :, 0].cuda()
+    dc.V[:, :, w.ctx0] = pre.v_next[:, :, 0].cuda()
+    pos0 = torch.full((w.batch,), w.ctx0, dtype=torch.int32, device="cuda")
+    tbl.project_keys(dc.shape, dc.K, dc.W, pos0, 1, dc.Kp)
+    K64[:, w.ctx0] = f64(pre.k_next[b][:, 0])
+    V64 = f64(pre.V[b])
+    V64[:, w.ctx0] = f64(pre.v_next[b][:, 0])
+    Kp_ref[:, w.ctx0] = orc.project(K64[:, w.ctx0], W64, dt)
+    np.testing.assert_array_equal(f64(dc.Kp[b][:, :ctx]), Kp_ref[:, :ctx])
+    # scores: bit-exact fp32
+    ctx_len = torch.full((w.batch,), ctx, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((w.batch, w.n_imp_heads, w.ctx_cap), dtype=torch.float32, device="cuda")
+    qi = pre.q_imp0.cuda()
+    tbl.score(dc.shape, qi, dc.Kp, ctx_len, scores, dc.ws)
+    s64, s32 = orc.score(f64(pre.q_imp0[b]), Kp_ref, n=ctx)
+    np.testing.assert_array_equal(scores[b, :, :ctx].cpu().numpy(), s32)
+    # the fp32 scores are within the fp64 rounding of the exact dot products
+    assert np.all(np.abs(s32.astype(np.float64) - s64) <= np.abs(s64) * 2.0 ** -24 + 1e-300)
+    # top-B and neighbor expansion: exact index sets
+    topb = torch.full((w.batch, w.n_imp_heads, w.budget), -1, dtype=torch.int32, device="cuda")
+    tbl.select(dc.shape, dc.params, scores, ctx_len, dc.sel, dc.cnt, dc.ws, topb_idx=topb)
+    torch.cuda.synchronize()
+    got = lists_of(dc.sel, dc.cnt, b)
+    S_ref = []
+    for i in range(w.n_imp_heads):
+        T_ref = orc.topb(s32[i], w.budget)
+        assert topb[b, i, :T_ref.size].cpu().tolist() == T_ref.tolist(), i
+        S_ref.append(orc.expand(T_ref, ctx, w.radius))
+        assert got[i] == S_ref[-1].tolist(), i
+    # attention over S united with the appended token
+    keep = torch.full((w.batch,), ctx - 1, dtype=torch.int32, device="cuda")
+    q = synth.draw_q(w, 0)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device="cuda")
+    tbl.sparse_attn(dc.shape, q.cuda(), dc.K, dc.V, dc.sel, dc.cap_s, dc.cnt, keep, ctx_len,
+                    w.softmax_scale, out, dc.ws)
+    torch.cuda.synchronize()
+    q64 = f64(q[b])
+    err = 0.0
+    for h in range(w.n_q_heads):
+        A = sorted(set(S_ref[_imp(w, h)].tolist()) | {ctx - 1})
+        ref = orc.attend(q64[h], K64[_kv(w, h)], V64[_kv(w, h)], A, w.softmax_scale)
+        err = max(err, float(np.abs(f64(out[b, h]) - ref).max()))
+    assert err <= TOL[w.dtype], err
+
+
+# --------------------------------------------------------------------------
+# the fused step at full size (the launch the benchmark times)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [TINY_F32, LLAMA_32K, LONG_128K], ids=lambda w: w.name)
+def test_fused_step_full_size(w):
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in range(w.batch):
+        st = oracle_state(w, dc.pre, b)
+        ref = oracle_step(w, st, dc.pre, inp, 0, b)
+        got = lists_of(dc.sel, dc.cnt, b)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        assert int(dc.keep[b]) == int(st.keep_from[0]) == w.ctx0
+        err = float(np.abs(f64(out[b]) - ref).max())
+        assert err <= TOL[w.dtype], err
+        # the projected-key cache, including the appended row, matches bit for bit
+        rows = np.random.default_rng(b).choice(w.ctx, size=min(w.ctx, 4096), replace=False)
+        rows[0] = w.ctx - 1
+        np.testing.assert_array_equal(f64(dc.Kp[b][:, rows]), st.Kp[:, rows])
+
+
+def test_planted_tokens_are_found():
+    # sanity of the synthetic workload, not a parity bar: with a shift of 4
+    # score standard deviations nearly every planted token is selected
+    w = TINY_F32
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    got = lists_of(dc.sel, dc.cnt, 0)
+    hit = sum(len(set(dc.pre.planted[(0, i)].tolist()) & set(got[i])) for i in range(4))
+    assert hit >= 28, hit
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_batched_32_layer_workload_sampled(layer):
+    # one layer of the batch-16 / 8K / radius-1 workload at full shape; the
+    # oracle checks sampled sequences of it
+    w = BATCHED_8K
+    dc = device_case(w, layer=layer)
+    inp = synth.step_inputs(w, 0, dc.pre, layer=layer)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in (0, 9, 15):
+        st = oracle_state(w, dc.pre, b)
+        ref = oracle_step(w, st, dc.pre, inp, 0, b)
+        got = lists_of(dc.sel, dc.cnt, b)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        err = float(np.abs(f64(out[b]) - ref).max())
+        assert err <= TOL[w.dtype], (b, err)
+    # every sequence: widened sets obey |S| <= (2r+1) B and contain T's size
+    cnt = dc.cnt.cpu().numpy()
+    assert cnt.max() <= 3 * w.budget and cnt.min() >= w.budget
+
+
+def test_prediction_interval_run():
+    # 64 steps, selection recomputed every 8 steps, radius 2, new tokens kept
+    w = INTERVAL_16K
+    dc = device_case(w)
+    check = (0, 3)
+    states = {b: oracle_state(w, dc.pre, b) for b in check}
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    worst = 0.0
+    for s in range(w.steps):
+        inp = synth.step_inputs(w, s, dc.pre)
+        step_on_device(dc, s, inp, out)
+        for b in check:
+            ref = oracle_step(w, states[b], dc.pre, inp, s, b)
+            worst = max(worst, float(np.abs(f64(out[b]) - ref).max()))
+            if inp.refresh:
+                got = lists_of(dc.sel, dc.cnt, b)
+                st = states[b]
+                for i in range(w.n_imp_heads):
+                    assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (s, b, i)
+            assert int(dc.keep[b]) == w.ctx0 + (s // w.interval) * w.interval
+    assert worst <= TOL[w.dtype], worst
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def _small(**kw) -> Workload:
+    base = dict(name="small", batch=3, layers=1, n_q_heads=8, n_kv_heads=2, n_imp_heads=8,
+                head_dim=128, d_imp=32, dtype="bf16", ctx0=1999, steps=1, budget=50, radius=1,
+                interval=1, plant_per_head=5, plant_runs=0, plant_run_len=0, plant_shift=3.0,
+                seed=11)
+    base.update(kw)
+    return Workload(**base)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(dtype="f32", head_dim=64, d_imp=16),
+    dict(n_imp_heads=2),                              # one importance head per KV head
+    dict(n_q_heads=16, n_kv_heads=2, n_imp_heads=4),  # group 8, importance heads shared by 4
+    dict(budget=1, radius=0),
+    dict(budget=3000),                                # budget >= context: dense
+    dict(radius=40),                                  # dilation in several passes
+    dict(n_q_heads=2, n_kv_heads=2, n_imp_heads=2, head_dim=64),
+], ids=["base", "f32", "imp_per_kv", "group8", "B1", "dense", "r40", "mha_d64"])
+def test_ragged_batch_fused(kw):
+    # three sequences of different lengths (1, 700 and 2000 tokens) in one launch
+    w = _small(**kw)
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    lens = [1, 700, 2000]
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    args = tbl.step_args(dc.shape, dc.params, q=inp.q.cuda(), q_imp=inp.q_imp.cuda(), k_new=inp.k_new.cuda(),
+                         v_new=inp.v_new.cuda(), refresh=True, w=dc.W, k_cache=dc.K,
+                         v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
+                         softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
+                         keep_from=dc.keep, out=out)
+    tbl.decode_step(dc.shape, dc.params, args, dc.ws)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        st = oracle_state(w, dc.pre, b)
+        ref = orc.decode_step(st, f64(dc.pre.W), f64(inp.q[b]), f64(inp.q_imp[b]), n, odtype(w),
+                              True, w.softmax_scale, k_new=f64(inp.k_new[b]),
+                              v_new=f64(inp.v_new[b]))
+        got = lists_of(dc.sel, dc.cnt, b)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        err = float(np.abs(f64(out[b]) - ref).max())
+        assert err <= TOL[w.dtype], (b, err)
+        if w.budget >= n:   # budget covering the context reproduces dense attention
+            for h in range(w.n_q_heads):
+                dense = orc.attend(f64(inp.q[b, h]), st.K[_kv(w, h)], st.V[_kv(w, h)],
+                                   np.arange(n), w.softmax_scale)
+                assert np.abs(f64(out[b, h]) - dense).max() <= TOL[w.dtype]
+
+
+def _select_case(scores_rows, lens, B, r):
+    """tb_select on crafted fp32 scores [b][H][cap]."""
+    bsz, H, cap = scores_rows.shape
+    shape = tbl.make_shape(bsz, H, H, H, 64, 16, cap, torch.float32)
+    params = tbl.make_params(B, r)
+    cap_s = tbl.selection_capacity(shape, params)
+    ws = tbl.alloc_workspace(shape, params)
+    sc = torch.from_numpy(np.ascontiguousarray(scores_rows, dtype=np.float32)).cuda()
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sel = torch.full((bsz, H, cap_s), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.full((bsz, H), -1, dtype=torch.int32, device="cuda")
+    topb = torch.full((bsz, H, B), -1, dtype=torch.int32, device="cuda")
+    tbl.select(shape, params, sc, ctx, sel, cnt, ws, topb_idx=topb)
+    torch.cuda.synchronize()
+    for b in range(bsz):
+        n = lens[b]
+        got = lists_of(sel, cnt, b)
+        for i in range(H):
+            T_ref = orc.topb(scores_rows[b, i, :n], B)
+            assert topb[b, i, :T_ref.size].cpu().tolist() == T_ref.tolist(), (b, i)
+            assert got[i] == orc.expand(T_ref, n, r).tolist(), (b, i)
+
+
+@pytest.mark.parametrize("B,r", [(1, 0), (5, 0), (37, 1), (100, 2), (700, 0), (64, 33)])
+def test_select_crafted_ties_and_signed_zeros(B, r):
+    rng = np.random.default_rng(B * 100 + r)
+    cap = 1500
+    rows = np.empty((3, 4, cap), dtype=np.float32)
+    rows[:, 0] = rng.standard_normal((3, cap))
+    rows[:, 1] = rng.integers(-3, 4, size=(3, cap))                    # heavy ties
+    rows[:, 2] = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(3, cap))
+    rows[:, 3] = 2.5                                                   # all equal
+    _select_case(rows, [1, 777, 1500], B, r)
+
+
+def test_select_single_and_empty_contexts():
+    rows = np.random.default_rng(5).standard_normal((2, 4, 64)).astype(np.float32)
+    _select_case(rows, [0, 1], 3, 1)
+
+
+def test_tie_heavy_scores_through_score_kernel():
+    # integer-valued projected keys and importance queries: many exact score
+    # ties, decided by position on both sides
+    w = _small(dtype="f32", head_dim=64, d_imp=16, budget=40, radius=1, plant_per_head=0)
+    pre = synth.prefill(w)
+    rng = np.random.default_rng(9)
+    K = np.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.head_dim), dtype=np.float32)
+    K[..., :w.d_imp] = rng.integers(-2, 3, size=K[..., :w.d_imp].shape)
+    Wm = np.zeros((w.head_dim, w.d_imp), dtype=np.float32)
+    Wm[np.arange(w.d_imp), np.arange(w.d_imp)] = 1.0
+    qi = rng.integers(-1, 2, size=(w.batch, w.n_imp_heads, w.d_imp)).astype(np.float32)
+    pre = replace(pre, K=torch.from_numpy(K), W=torch.from_numpy(Wm), q_imp0=torch.from_numpy(qi),
+                  k_next=torch.from_numpy(K[:, :, w.ctx0:w.ctx0 + 1].copy()))
+    dc = device_case(w, pre=pre)
+    inp = synth.step_inputs(w, 0, pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in range(w.batch):
+        st = oracle_state(w, pre, b)
+        ref = oracle_step(w, st, pre, inp, 0, b)
+        got = lists_of(dc.sel, dc.cnt, b)
+        _, s32 = orc.score(qi[b].astype(np.float64), st.Kp, n=w.ctx)
+        assert band_members(s32[0], w.budget).size > 1   # the case really has ties at tau
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        assert float(np.abs(f64(out[b]) - ref).max()) <= TOL["f32"]
+
+
+def test_empty_attended_set_gives_zero_rows():
+    w = _small(batch=2)
+    dc = device_case(w)
+    q = synth.draw_q(w, 0).cuda()
+    dc.cnt.zero_()
+    ctx = torch.tensor([0, 1500], dtype=torch.int32, device="cuda")
+    out = torch.full((w.batch, w.n_q_heads, w.head_dim), 7.0, dtype=dc.K.dtype, device="cuda")
+    tbl.sparse_attn(dc.shape, q, dc.K, dc.V, dc.sel, dc.cap_s, dc.cnt, None, ctx,
+                    w.softmax_scale, out, dc.ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+
+
+def test_attention_ignores_list_entries_beyond_context():
+    # a stored list may hold positions of a longer context; only [0, n) counts
+    w = _small(batch=1, ctx0=999)
+    dc = device_case(w)
+    q = synth.draw_q(w, 0)
+    lst = np.array([3, 10, 500, 998, 999], dtype=np.int32)
+    dc.sel.fill_(0)
+    dc.sel[0, :, :lst.size] = torch.from_numpy(lst).cuda()
+    dc.cnt.fill_(lst.size)
+    ctx = torch.tensor([600], dtype=torch.int32, device="cuda")
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    tbl.sparse_attn(dc.shape, q.cuda(), dc.K, dc.V, dc.sel, dc.cap_s, dc.cnt, None, ctx,
+                    w.softmax_scale, out, dc.ws)
+    torch.cuda.synchronize()
+    K64, V64 = f64(dc.pre.K[0]), f64(dc.pre.V[0])
+    for h in range(w.n_q_heads):
+        ref = orc.attend(f64(q[0, h]), K64[_kv(w, h)], V64[_kv(w, h)], [3, 10, 500],
+                         w.softmax_scale)
+        assert np.abs(f64(out[0, h]) - ref).max() <= TOL["bf16"]
+
+
+def test_fused_step_is_deterministic():
+    w = LLAMA_32K
+    outs = []
+    for _ in range(2):
+        dc = device_case(w)
+        inp = synth.step_inputs(w, 0, dc.pre)
+        out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+        step_on_device(dc, 0, inp, out)
+        outs.append((out.clone(), dc.sel.clone(), dc.cnt.clone(), dc.Kp.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
