@@ -124,6 +124,8 @@ def main() -> int:
             K=K0.clone(), V=V0.clone(), Kp=Kp0.clone(),
             sel=torch.zeros((w.batch, w.n_imp_heads, cap_s), dtype=torch.int32, device=dev),
             cnt=torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev),
+            bits=torch.zeros((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)),
+                             dtype=torch.int32, device=dev),
             keep=torch.zeros(w.batch, dtype=torch.int32, device=dev)))
     del K0, V0, Kp0
     ws = tbl.alloc_workspace(shape, params, dev)
@@ -134,7 +136,8 @@ def main() -> int:
     step_args = [tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=True, w=W,
                                k_cache=r["K"], v_cache=r["V"], kp_cache=r["Kp"], ctx_len=ctx,
                                softmax_scale=w.softmax_scale, sel_idx=r["sel"],
-                               sel_count=r["cnt"], keep_from=r["keep"], out=out)
+                               sel_count=r["cnt"], sel_bits=r["bits"], keep_from=r["keep"],
+                               out=out)
                  for r in reps]
     torch.cuda.synchronize()
 
@@ -156,14 +159,14 @@ def main() -> int:
     # dominant kernel: the gathered attention, launched alone on the same stream
     for s in range(a.warmup):
         r = reps[s % R]
-        tbl.sparse_attn(shape, q, r["K"], r["V"], r["sel"], cap_s, r["cnt"], r["keep"], ctx,
-                        w.softmax_scale, out, ws)
+        tbl.sparse_attn(shape, q, r["K"], r["V"], None, 0, None, r["keep"], ctx,
+                        w.softmax_scale, out, ws, sel_bits=r["bits"])
     torch.cuda.synchronize()
     e0.record(stream)
     for s in range(a.steps):
         r = reps[s % R]
-        tbl.sparse_attn(shape, q, r["K"], r["V"], r["sel"], cap_s, r["cnt"], r["keep"], ctx,
-                        w.softmax_scale, out, ws)
+        tbl.sparse_attn(shape, q, r["K"], r["V"], None, 0, None, r["keep"], ctx,
+                        w.softmax_scale, out, ws, sel_bits=r["bits"])
     e1.record(stream)
     torch.cuda.synchronize()
     ms_attn = e0.elapsed_time(e1) / a.steps

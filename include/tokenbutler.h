@@ -36,6 +36,8 @@
  *     scores       [batch][n_imp_heads][ctx_cap]
  *     sel_idx      [batch][n_imp_heads][sel_stride]  ascending positions
  *     sel_count    [batch][n_imp_heads]
+ *     sel_bits     [batch][n_imp_heads][tb_bitmap_words()]  bit t%32 of word
+ *                  t/32 set iff position t is selected
  *     ctx_len, keep_from, pos0   [batch]
  *     out          [batch][n_q_heads][head_dim]
  * - Head maps: query head h reads KV head h*Hkv/Hq and importance head
@@ -106,6 +108,10 @@ size_t tb_workspace_bytes(const tb_shape *shape, const tb_select_params *params)
  * sel_idx stride written by tb_select and tb_decode_step.  0 if invalid. */
 int32_t tb_selection_capacity(const tb_shape *shape, const tb_select_params *params);
 
+/* 32-bit words of one head's selection bitmap: ceil(ctx_cap / 32).  0 if the
+ * shape is invalid. */
+int32_t tb_bitmap_words(const tb_shape *shape);
+
 /*
  * tb_project_keys -- append-time key projection into the projected-key cache.
  * [ARCH]: the real cache keys are mapped into the low-dimensional importance
@@ -144,12 +150,14 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
  *   S = union over t in T of [max(0, t-r), min(n-1, t+r)].
  * sel_idx[b][i][0 .. |S|) receives S ascending (stride
  * tb_selection_capacity()), sel_count[b][i] = |S|.  If topb_idx is not NULL
- * it receives T ascending with stride B (its count is min(B, n)).
+ * it receives T ascending with stride B (its count is min(B, n)).  If
+ * sel_bits is not NULL it receives S as a bitmap (all tb_bitmap_words()
+ * words of the head are written; bits at positions >= n are zero).
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
               const int32_t *ctx_len, int32_t *sel_idx, int32_t *sel_count, int32_t *topb_idx,
-              void *ws, size_t ws_bytes, void *stream);
+              uint32_t *sel_bits, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * tb_sparse_attn -- exact softmax attention over the selected rows only.
@@ -163,13 +171,16 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
  * and out[b][h] = sum_{t in A} softmax_t(scale * q[b][h] . K[b][g][t]) V[b][g][t],
  * accumulated in fp32 and rounded to the dtype.  An empty A gives a zero row.
  * sel_idx lists must be ascending and duplicate-free; sel_count is clamped to
- * sel_stride.  Rows shared by several query heads of one KV head are read
- * once.  Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ * sel_stride.  When sel_bits is not NULL the selected set is read from that
+ * bitmap instead and sel_idx / sel_count are ignored (they may be NULL).
+ * Rows shared by several query heads of one KV head are read once.
+ * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
                    const void *v_cache, const int32_t *sel_idx, int32_t sel_stride,
-                   const int32_t *sel_count, const int32_t *keep_from, const int32_t *ctx_len,
-                   float softmax_scale, void *out, void *ws, size_t ws_bytes, void *stream);
+                   const int32_t *sel_count, const uint32_t *sel_bits, const int32_t *keep_from,
+                   const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
+                   size_t ws_bytes, void *stream);
 
 /* Arguments of one fused decode step (all pointers device pointers). */
 typedef struct tb_step_args {
@@ -187,6 +198,7 @@ typedef struct tb_step_args {
     float softmax_scale;
     int32_t *sel_idx;     /* state [b][Himp][tb_selection_capacity()] */
     int32_t *sel_count;   /* state [b][Himp] */
+    uint32_t *sel_bits;   /* state [b][Himp][tb_bitmap_words()] */
     int32_t *keep_from;   /* state [b] */
     void *out;            /* [b][Hq][D] */
 } tb_step_args;
@@ -202,12 +214,13 @@ typedef struct tb_step_args {
  *    [ctx_len[b] - n_new, ctx_len[b]) of the caches and their keys projected
  *    (as tb_project_keys).
  * 2. If refresh: scores over [0, ctx_len[b]) (as tb_score), T and S (as
- *    tb_select) are stored in sel_idx / sel_count, and
+ *    tb_select) are stored in sel_idx / sel_count / sel_bits, and
  *    keep_from[b] = ctx_len[b] - n_new.
  * 3. out = attention over S united with [keep_from[b], ctx_len[b]) (as
  *    tb_sparse_attn), so tokens appended since the last refresh are always
  *    attended.
- * On a non-refresh step the state is read, not written.  ctx_len[b] - n_new
+ * On a non-refresh step the state (sel_bits and keep_from) is read, not
+ * written.  ctx_len[b] - n_new
  * must be >= 0.  Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,

@@ -63,14 +63,16 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? TB_OK : TB_EHIP; }
 struct Ws {
     double *q64;
     float *scores;
-    float *part;
+    float *part_o;
+    float *part_ml;
     uint32_t *counters;
 };
 
 Ws carve(void *ws, const WsLayout &L)
 {
     char *base = (char *)ws;
-    return Ws{(double *)(base + L.qimp64), (float *)(base + L.scores), (float *)(base + L.part),
+    return Ws{(double *)(base + L.qimp64), (float *)(base + L.scores),
+              (float *)(base + L.part_o), (float *)(base + L.part_ml),
               (uint32_t *)(base + L.counters)};
 }
 
@@ -125,6 +127,13 @@ int32_t tb_selection_capacity(const tb_shape *shape, const tb_select_params *par
     return sel_capacity(*shape, *params);
 }
 
+int32_t tb_bitmap_words(const tb_shape *shape)
+{
+    if (check_shape(shape) != TB_OK)
+        return 0;
+    return bitmap_words(shape->ctx_cap);
+}
+
 int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
                     const int32_t *pos0, int32_t n_tokens, void *kp_cache, void *stream)
 {
@@ -160,7 +169,7 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
 
 int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
               const int32_t *ctx_len, int32_t *sel_idx, int32_t *sel_count, int32_t *topb_idx,
-              void *ws, size_t ws_bytes, void *stream)
+              uint32_t *sel_bits, void *ws, size_t ws_bytes, void *stream)
 {
     TB_TRY(check_shape(shape));
     TB_TRY(check_params(params));
@@ -169,18 +178,21 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
-                                sel_capacity(*shape, *params), sel_count, topb_idx,
+                                sel_capacity(*shape, *params), sel_count, topb_idx, sel_bits,
                                 (hipStream_t)stream));
 }
 
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
                    const void *v_cache, const int32_t *sel_idx, int32_t sel_stride,
-                   const int32_t *sel_count, const int32_t *keep_from, const int32_t *ctx_len,
-                   float softmax_scale, void *out, void *ws, size_t ws_bytes, void *stream)
+                   const int32_t *sel_count, const uint32_t *sel_bits, const int32_t *keep_from,
+                   const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
+                   size_t ws_bytes, void *stream)
 {
     TB_TRY(check_shape(shape));
-    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || sel_idx == nullptr ||
-        sel_count == nullptr || ctx_len == nullptr || out == nullptr || sel_stride <= 0)
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || ctx_len == nullptr ||
+        out == nullptr)
+        return TB_EINVAL;
+    if (sel_bits == nullptr && (sel_idx == nullptr || sel_count == nullptr || sel_stride <= 0))
         return TB_EINVAL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return TB_EINVAL;
@@ -190,8 +202,8 @@ int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     Ws W = carve(ws, L);
     return hip_rc(launch_attn(*shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count,
-                              keep_from, ctx_len, softmax_scale, out, W.part, W.counters,
-                              (hipStream_t)stream));
+                              sel_bits, keep_from, ctx_len, softmax_scale, out, W.part_o,
+                              W.part_ml, W.counters, (hipStream_t)stream));
 }
 
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
@@ -203,7 +215,8 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
         return TB_EINVAL;
     if (a->q == nullptr || a->w == nullptr || a->k_cache == nullptr || a->v_cache == nullptr ||
         a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_idx == nullptr ||
-        a->sel_count == nullptr || a->keep_from == nullptr || a->out == nullptr)
+        a->sel_count == nullptr || a->sel_bits == nullptr || a->keep_from == nullptr ||
+        a->out == nullptr)
         return TB_EINVAL;
     if (a->n_new < 0 || (a->n_new > 0 && (a->k_new == nullptr || a->v_new == nullptr)))
         return TB_EINVAL;
@@ -229,11 +242,11 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                                       a->keep_from, st)));
         TB_TRY(hip_rc(launch_score(*shape, W.q64, a->kp_cache, a->ctx_len, W.scores, st)));
         TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
-                                    a->sel_count, nullptr, st)));
+                                    a->sel_count, nullptr, a->sel_bits, st)));
     }
     return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
-                              a->sel_count, a->keep_from, a->ctx_len, a->softmax_scale, a->out,
-                              W.part, W.counters, st));
+                              a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,
+                              a->softmax_scale, a->out, W.part_o, W.part_ml, W.counters, st));
 }
 
 } // extern "C"

@@ -78,7 +78,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
 // ---------------------------------------------------------------- sizes
-constexpr int kAttnChunk = 512;     // positions per attention work-group
+constexpr int kAttnChunk = 1024;    // positions per attention work-group
 constexpr int kMaxCtxCap = 262144;  // bounded by the selection kernel's LDS bitmaps
 constexpr size_t kAlign = 256;
 
@@ -88,12 +88,14 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct WsLayout {
     size_t qimp64;   // fp64 copy of q_imp [b][Himp][d]
     size_t scores;   // fp32 scores [b][Himp][cap] (fused step only)
-    size_t part;     // attention partials [b][Hq][nchunk][D + 2] fp32
+    size_t part_o;   // attention partial sums [b][Hq][nchunk][D] fp32
+    size_t part_ml;  // attention partial (max, sum) [b][Hq][nchunk][2] fp32
     size_t counters; // attention arrival counters [b][Hkv] u32 (kept zero)
     size_t total;
 };
 
 inline int attn_chunks(int cap) { return (cap + kAttnChunk - 1) / kAttnChunk; }
+inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 
 inline WsLayout ws_layout(const tb_shape &s)
 {
@@ -103,9 +105,11 @@ inline WsLayout ws_layout(const tb_shape &s)
     off += align_up((size_t)s.batch * s.n_imp_heads * s.d_imp * sizeof(double));
     L.scores = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(float));
-    L.part = off;
-    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * (s.head_dim + 2) *
+    L.part_o = off;
+    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * s.head_dim *
                     sizeof(float));
+    L.part_ml = off;
+    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * 2 * sizeof(float));
     L.counters = off;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
     L.total = off;
@@ -126,11 +130,13 @@ hipError_t launch_score(const tb_shape &s, const double *q64, const void *kp_cac
                         const int32_t *ctx_len, float *scores, hipStream_t st);
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
-                         int32_t *sel_count, int32_t *topb_idx, hipStream_t st);
+                         int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
+                         hipStream_t st);
 hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *sel_idx, int sel_stride,
-                       const int32_t *sel_count, const int32_t *keep_from,
-                       const int32_t *ctx_len, float softmax_scale, void *out, float *part,
-                       uint32_t *counters, hipStream_t st);
+                       const int32_t *sel_count, const uint32_t *sel_bits,
+                       const int32_t *keep_from, const int32_t *ctx_len, float softmax_scale,
+                       void *out, float *part_o, float *part_ml, uint32_t *counters,
+                       hipStream_t st);
 
 } // namespace tb

@@ -6,19 +6,21 @@
 // fetching widens each kept token t to [t-r, t+r].
 //
 // One 1024-thread work-group per (sequence, importance head):
-//   1. Scores become order-preserving u32 keys (-0 folded onto +0).
-//   2. Radix select, 4 passes of 8 bits from the top: per-wave LDS histograms
-//      of the keys that match the prefix found so far, then a wave-wide
-//      suffix scan picks the digit holding the B-th largest key.  This yields
-//      the threshold key tau and how many of the keys equal to tau are kept
-//      (the lowest positions first).
-//   3. A ballot pass writes the kept set T as a bitmap in LDS; a block scan of
+//   1. Scores become order-preserving u32 keys (-0 folded onto +0).  Up to
+//      64 keys per thread stay in registers, so the scores are read once.
+//   2. Radix select from the top, 8 bits per pass, over the keys that match
+//      the prefix found so far.  Histograms live in LDS as 16 copies (lane
+//      mod 16), padded so that equal digits in different copies fall in
+//      different banks: at most four lanes of a wave hit one address.  A
+//      wave-wide suffix scan picks the digit holding the B-th largest key.
+//      When every key of that digit is needed the search stops early.
+//      Result: the threshold tau and how many keys equal to it are kept (the
+//      lowest positions first).
+//   3. A ballot pass writes the kept set T as an LDS bitmap; a block scan of
 //      per-word tie counts settles ties at tau by position.
-//   4. Dilation by r is word-wise shifts of the bitmap (clipped to [0, n)).
+//   4. Dilation by r is word-wise shifts of the bitmap, clipped to [0, n).
 //   5. A block scan of per-word popcounts compacts the bitmap into the
-//      ascending index list.
-// When every key fits in registers (n <= 64 per thread) the scores are read
-// from memory once; otherwise every pass streams them again.
+//      ascending index list; the bitmap itself can be written out too.
 #include "tb_internal.h"
 
 namespace tb {
@@ -26,6 +28,8 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kCopies = 16;
+constexpr int kCopyStride = 257; // words; the odd stride spreads copies over banks
 
 __device__ __forceinline__ uint32_t score_key(float s)
 {
@@ -35,8 +39,8 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of popcount(words[w]) over w < nw into out[w]; returns
-// the total to every thread.  wsum: kSelWaves + 1 words of LDS scratch.
+// Exclusive scan of popcount(words[w]) over w < nw into out[w]; returns the
+// total to every thread.  wsum: kSelWaves + 1 words of LDS scratch.
 __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int nw,
                                       uint32_t *wsum)
 {
@@ -46,7 +50,6 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
     uint32_t local = 0;
     for (int w = w0; w < w0 + per && w < nw; ++w)
         local += __popc(words[w]);
-    // inclusive scan within the wave
     uint32_t inc = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -58,7 +61,7 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
         wsum[wave] = inc;
     __syncthreads();
     if (wave == 0) {
-        uint32_t v = lane < kSelWaves ? wsum[lane] : 0u;
+        const uint32_t v = lane < kSelWaves ? wsum[lane] : 0u;
         uint32_t x = v;
 #pragma unroll
         for (int off = 1; off < kSelWaves; off <<= 1) {
@@ -100,15 +103,17 @@ template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
     int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
-    int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx)
+    int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
+    uint32_t *__restrict__ sel_bits, int bits_stride)
 {
     extern __shared__ uint32_t lds[];
-    uint32_t *hist = lds;                      // [kSelWaves][256]
-    uint32_t *misc = hist + kSelWaves * 256;   // 64 words
-    uint32_t *Tb = misc + 64;                  // [nwc] kept set
-    uint32_t *Sb = Tb + nwc;                   // [nwc] widened set / tie bits
-    uint32_t *Xb = Sb + nwc;                   // [nwc] dilation ping-pong
-    uint32_t *scan = Xb + nwc;                 // [nwc] scan output
+    uint32_t *hist = lds;                         // [kCopies][kCopyStride]
+    uint32_t *tot = hist + kCopies * kCopyStride; // [256]
+    uint32_t *misc = tot + 256;                   // 64 words
+    uint32_t *Tb = misc + 64;                     // [nwc] kept set
+    uint32_t *Sb = Tb + nwc;                      // [nwc] widened set / tie bits
+    uint32_t *Xb = Sb + nwc;                      // [nwc] dilation ping-pong
+    uint32_t *scan = Xb + nwc;                    // [nwc] scan output
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y, i = blockIdx.x;
@@ -119,12 +124,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (n == 0) {
         if (tid == 0)
             sel_count[rowid] = 0;
+        if (sel_bits != nullptr)
+            for (int w = tid; w < bits_stride; w += kSelThreads)
+                sel_bits[rowid * bits_stride + w] = 0u;
         return;
     }
     const int nw = (n + 31) >> 5;
     const int nk = (n + kSelThreads - 1) / kSelThreads;
 
-    // Keys of this thread: keys[k] belongs to position k * kSelThreads + tid.
+    // keys[k] belongs to position k * kSelThreads + tid
     constexpr int KR = KPT > 0 ? KPT : 1;
     uint32_t keys[KR];
     if constexpr (KPT > 0) {
@@ -136,15 +144,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
 
     const bool take_all = B >= n;
-    uint32_t tau = 0u, need = 0u, cnt_eq = 0u;
+    uint32_t tau = 0u, fmask = 0u, need = 0u, cnt_eq = 0u;
     if (!take_all) {
+        for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+            hist[e] = 0u;
+        __syncthreads();
         uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
+        uint32_t *h = hist + (lane & (kCopies - 1)) * kCopyStride;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            for (int e = tid; e < kSelWaves * 256; e += kSelThreads)
-                hist[e] = 0u;
-            __syncthreads();
-            uint32_t *h = hist + wave * 256;
             if constexpr (KPT > 0) {
 #pragma unroll
                 for (int k = 0; k < KR; ++k) {
@@ -165,16 +173,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             }
             __syncthreads();
             if (tid < 256) {
-                uint32_t c = 0u;
+                uint32_t cnt = 0u;
 #pragma unroll
-                for (int w = 0; w < kSelWaves; ++w)
-                    c += hist[w * 256 + tid];
-                hist[tid] = c;
+                for (int cp = 0; cp < kCopies; ++cp) {
+                    cnt += hist[cp * kCopyStride + tid];
+                    hist[cp * kCopyStride + tid] = 0u; // ready for the next pass
+                }
+                tot[tid] = cnt;
             }
             __syncthreads();
             if (wave == 0) {
-                const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1];
-                const uint32_t c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+                const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1];
+                const uint32_t c2 = tot[4 * lane + 2], c3 = tot[4 * lane + 3];
                 const uint32_t sl = c0 + c1 + c2 + c3;
                 uint32_t suf = sl; // inclusive suffix sum over lanes
 #pragma unroll
@@ -214,10 +224,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             krem = misc[1];
             cnt_eq = misc[2];
             pmask |= 255u << shift;
-            __syncthreads();
+            if (krem == cnt_eq)
+                break; // every key with this prefix is kept
         }
         tau = prefix;
-        need = krem; // keys equal to tau that are kept, lowest positions first
+        fmask = pmask;
+        need = krem; // keys equal to tau (under fmask) kept, lowest positions first
     }
     const bool partial_ties = !take_all && need < cnt_eq;
 
@@ -225,8 +237,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     auto emit = [&](int k, uint32_t key) {
         const int t = k * kSelThreads + tid;
         const bool valid = t < n;
-        const bool gt = valid && (take_all || key > tau || (!partial_ties && key == tau));
-        const bool eq = valid && partial_ties && key == tau;
+        const uint32_t km = key & fmask;
+        const bool gt = valid && (take_all || km > tau || (!partial_ties && km == tau));
+        const bool eq = valid && partial_ties && km == tau;
         const unsigned long long mg = __ballot(gt);
         const unsigned long long me = __ballot(eq);
         const int w0 = (k * kSelThreads + wave * 64) >> 5;
@@ -302,9 +315,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
 
-    // ---- compaction into the ascending list ----
+    // ---- compaction into the ascending list (and the bitmap, if asked) ----
     const uint32_t total = block_popc_exscan(fin, scan, nw, misc + 8);
     compact_bits(fin, scan, nw, out_sel);
+    if (sel_bits != nullptr)
+        for (int w = tid; w < bits_stride; w += kSelThreads)
+            sel_bits[rowid * bits_stride + w] = w < nw ? fin[w] : 0u;
     if (tid == 0)
         sel_count[rowid] = (int32_t)total;
 }
@@ -312,10 +328,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 template <int KPT>
 hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
-                    int32_t *sel_count, int32_t *topb_idx, hipStream_t st)
+                    int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits, hipStream_t st)
 {
     const int nwc = (s.ctx_cap + 31) / 32 + 1;
-    const size_t lds = ((size_t)kSelWaves * 256 + 64 + 4 * (size_t)nwc) * sizeof(uint32_t);
+    const size_t lds =
+        ((size_t)kCopies * kCopyStride + 256 + 64 + 4 * (size_t)nwc) * sizeof(uint32_t);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)select_kernel<KPT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -325,7 +342,7 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
     dim3 grid(s.n_imp_heads, s.batch);
     hipLaunchKernelGGL(select_kernel<KPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
                        s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx, sel_stride,
-                       sel_count, topb_idx);
+                       sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap));
     return hipGetLastError();
 }
 
@@ -333,16 +350,20 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
 
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
-                         int32_t *sel_count, int32_t *topb_idx, hipStream_t st)
+                         int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
+                         hipStream_t st)
 {
+#define TB_SEL_ARGS s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, st
     const int per = (s.ctx_cap + kSelThreads - 1) / kSelThreads;
-    if (per <= 1) return select_t<1>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    if (per <= 2) return select_t<2>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    if (per <= 4) return select_t<4>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    if (per <= 8) return select_t<8>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    if (per <= 16) return select_t<16>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    if (per <= 32) return select_t<32>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
-    return select_t<0>(s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, st);
+    if (per <= 1) return select_t<1>(TB_SEL_ARGS);
+    if (per <= 2) return select_t<2>(TB_SEL_ARGS);
+    if (per <= 4) return select_t<4>(TB_SEL_ARGS);
+    if (per <= 8) return select_t<8>(TB_SEL_ARGS);
+    if (per <= 16) return select_t<16>(TB_SEL_ARGS);
+    if (per <= 32) return select_t<32>(TB_SEL_ARGS);
+    if (per <= 64) return select_t<64>(TB_SEL_ARGS);
+    return select_t<0>(TB_SEL_ARGS);
+#undef TB_SEL_ARGS
 }
 
 } // namespace tb

@@ -37,7 +37,7 @@ class StepArgs(ctypes.Structure):
                 ("n_new", _i32), ("refresh", _i32), ("w", _vp), ("k_cache", _vp),
                 ("v_cache", _vp), ("kp_cache", _vp), ("ctx_len", _vp),
                 ("softmax_scale", ctypes.c_float), ("sel_idx", _vp), ("sel_count", _vp),
-                ("keep_from", _vp), ("out", _vp)]
+                ("sel_bits", _vp), ("keep_from", _vp), ("out", _vp)]
 
 
 class TokenButlerError(RuntimeError):
@@ -66,11 +66,13 @@ def lib() -> ctypes.CDLL:
         L.tb_workspace_bytes.argtypes = [P(Shape), P(SelectParams)]
         L.tb_selection_capacity.restype = _i32
         L.tb_selection_capacity.argtypes = [P(Shape), P(SelectParams)]
+        L.tb_bitmap_words.restype = _i32
+        L.tb_bitmap_words.argtypes = [P(Shape)]
         L.tb_project_keys.argtypes = [P(Shape), _vp, _vp, _vp, _i32, _vp, _vp]
         L.tb_score.argtypes = [P(Shape), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-        L.tb_select.argtypes = [P(Shape), P(SelectParams), _vp, _vp, _vp, _vp, _vp, _vp,
+        L.tb_select.argtypes = [P(Shape), P(SelectParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]
-        L.tb_sparse_attn.argtypes = [P(Shape), _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp,
+        L.tb_sparse_attn.argtypes = [P(Shape), _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                      ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
         L.tb_decode_step.argtypes = [P(Shape), P(SelectParams), P(StepArgs), _vp,
                                      ctypes.c_size_t, _vp]
@@ -146,6 +148,10 @@ def selection_capacity(shape: Shape, params: SelectParams) -> int:
     return int(lib().tb_selection_capacity(ctypes.byref(shape), ctypes.byref(params)))
 
 
+def bitmap_words(shape: Shape) -> int:
+    return int(lib().tb_bitmap_words(ctypes.byref(shape)))
+
+
 def alloc_workspace(shape: Shape, params: SelectParams | None = None, device="cuda"):
     """A zero-filled workspace of the size the library asks for."""
     n = workspace_bytes(shape, params)
@@ -176,21 +182,25 @@ def score(shape, q_imp, kp_cache, ctx_len, scores, ws, stream=None):
         _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
-def select(shape, params, scores, ctx_len, sel_idx, sel_count, ws, topb_idx=None, stream=None):
+def select(shape, params, scores, ctx_len, sel_idx, sel_count, ws, topb_idx=None,
+           sel_bits=None, stream=None):
     rows = shape.batch * shape.n_imp_heads
     _expect("scores", scores, rows * shape.ctx_cap, torch.float32)
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _expect("sel_idx", sel_idx, rows * selection_capacity(shape, params), torch.int32)
     _expect("sel_count", sel_count, rows, torch.int32)
     _expect("topb_idx", topb_idx, rows * params.budget, torch.int32)
+    _expect("sel_bits", sel_bits, rows * bitmap_words(shape), torch.int32)
     _check("tb_select", lib().tb_select(
         ctypes.byref(shape), ctypes.byref(params), _ptr(scores), _ptr(ctx_len), _ptr(sel_idx),
-        _ptr(sel_count), _ptr(topb_idx), _ptr(ws), ws.numel() if ws is not None else 0,
-        _stream(stream)))
+        _ptr(sel_count), _ptr(topb_idx), _ptr(sel_bits), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def sparse_attn(shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count, keep_from, ctx_len,
-                softmax_scale, out, ws, stream=None):
+                softmax_scale, out, ws, sel_bits=None, stream=None):
+    """Attention over the selected rows; membership from sel_bits when given,
+    else from the sel_idx / sel_count lists."""
     e = _elt(shape)
     rows = shape.batch * shape.n_imp_heads
     qn = shape.batch * shape.n_q_heads * shape.head_dim
@@ -198,19 +208,21 @@ def sparse_attn(shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count, keep
     _expect("out", out, qn, e)
     _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
     _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e)
-    _expect("sel_idx", sel_idx, rows * int(sel_stride), torch.int32)
+    if sel_idx is not None:
+        _expect("sel_idx", sel_idx, rows * int(sel_stride), torch.int32)
     _expect("sel_count", sel_count, rows, torch.int32)
+    _expect("sel_bits", sel_bits, rows * bitmap_words(shape), torch.int32)
     _expect("keep_from", keep_from, shape.batch, torch.int32)
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _check("tb_sparse_attn", lib().tb_sparse_attn(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx),
-        int(sel_stride), _ptr(sel_count), _ptr(keep_from), _ptr(ctx_len),
+        int(sel_stride), _ptr(sel_count), _ptr(sel_bits), _ptr(keep_from), _ptr(ctx_len),
         float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
 
 
 def step_args(shape, params, *, q, q_imp, k_new, v_new, refresh, w, k_cache, v_cache, kp_cache,
-              ctx_len, softmax_scale, sel_idx, sel_count, keep_from, out) -> StepArgs:
+              ctx_len, softmax_scale, sel_idx, sel_count, sel_bits, keep_from, out) -> StepArgs:
     """Pointers of one fused step, after checking every tensor's size.  The
     tensors must stay alive until the step has run."""
     n_new = 0 if k_new is None else int(k_new.shape[2])
@@ -229,14 +241,15 @@ def step_args(shape, params, *, q, q_imp, k_new, v_new, refresh, w, k_cache, v_c
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _expect("sel_idx", sel_idx, rows * selection_capacity(shape, params), torch.int32)
     _expect("sel_count", sel_count, rows, torch.int32)
+    _expect("sel_bits", sel_bits, rows * bitmap_words(shape), torch.int32)
     _expect("keep_from", keep_from, shape.batch, torch.int32)
     a = StepArgs()
     a.q, a.q_imp, a.k_new, a.v_new = _ptr(q), _ptr(q_imp), _ptr(k_new), _ptr(v_new)
     a.n_new, a.refresh = n_new, int(bool(refresh))
     a.w, a.k_cache, a.v_cache, a.kp_cache = _ptr(w), _ptr(k_cache), _ptr(v_cache), _ptr(kp_cache)
     a.ctx_len, a.softmax_scale = _ptr(ctx_len), float(softmax_scale)
-    a.sel_idx, a.sel_count, a.keep_from, a.out = (_ptr(sel_idx), _ptr(sel_count),
-                                                  _ptr(keep_from), _ptr(out))
+    a.sel_idx, a.sel_count, a.sel_bits = _ptr(sel_idx), _ptr(sel_count), _ptr(sel_bits)
+    a.keep_from, a.out = _ptr(keep_from), _ptr(out)
     return a
 
 

@@ -47,6 +47,7 @@ class DeviceCase:
     ws: torch.Tensor
     sel: torch.Tensor
     cnt: torch.Tensor
+    bits: torch.Tensor
     keep: torch.Tensor
 
 
@@ -71,8 +72,10 @@ def device_case(w: Workload, layer: int = 0, pre: synth.Prefill | None = None) -
     ws = tbl.alloc_workspace(shape, params, dev)
     sel = torch.full((w.batch, w.n_imp_heads, cap_s), -1, dtype=torch.int32, device=dev)
     cnt = torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev)
+    bits = torch.zeros((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)), dtype=torch.int32,
+                       device=dev)
     keep = torch.zeros(w.batch, dtype=torch.int32, device=dev)
-    return DeviceCase(w, pre, shape, params, cap_s, K, V, Kp, W, ws, sel, cnt, keep)
+    return DeviceCase(w, pre, shape, params, cap_s, K, V, Kp, W, ws, sel, cnt, bits, keep)
 
 
 def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Tensor):
@@ -86,7 +89,7 @@ def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Ten
     args = tbl.step_args(dc.shape, dc.params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=inp.refresh, w=dc.W,
                          k_cache=dc.K, v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
                          softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
-                         keep_from=dc.keep, out=out)
+                         sel_bits=dc.bits, keep_from=dc.keep, out=out)
     tbl.decode_step(dc.shape, dc.params, args, dc.ws)
     torch.cuda.synchronize()
     return ctx
@@ -113,6 +116,16 @@ def lists_of(sel: torch.Tensor, cnt: torch.Tensor, b: int) -> list:
     s = sel[b].cpu().numpy()
     c = cnt[b].cpu().numpy()
     return [s[i, :c[i]].tolist() for i in range(s.shape[0])]
+
+
+def bitmap_positions(bits: torch.Tensor, b: int, n: int) -> list:
+    """Per head, the positions whose bit is set in a selection bitmap."""
+    words = bits[b].cpu().numpy().view(np.uint32)
+    out = []
+    for row in words:
+        bitsu8 = np.unpackbits(row.view(np.uint8), bitorder="little")
+        out.append(np.nonzero(bitsu8)[0].tolist())
+    return out
 
 
 def band_members(s32: np.ndarray, B: int, rel: float = 1e-6) -> np.ndarray:

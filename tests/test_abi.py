@@ -61,6 +61,8 @@ def test_workspace_and_capacity():
     assert tbl.selection_capacity(s, p) == 3277
     assert tbl.selection_capacity(s, tbl.make_params(3277, 1)) == 3 * 3277
     assert tbl.selection_capacity(_shape(ctx_cap=1000), tbl.make_params(600, 2)) == 1000
+    assert tbl.bitmap_words(_shape(ctx_cap=1000)) == 32
+    assert tbl.bitmap_words(_shape(ctx_cap=1024)) == 32
     assert tbl.workspace_bytes(_shape(head_dim=96), p) == 0
     assert tbl.workspace_bytes(_shape(n_q_heads=12), p) == 0
 
@@ -90,16 +92,19 @@ def test_null_pointers_and_params_rejected():
     fake = ctypes.c_void_p(1 << 20)
     assert L.tb_score(ctypes.byref(s), None, fake, fake, fake, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(0, 0)), fake, fake, fake,
-                       fake, None, fake, 1 << 30, None) == tbl.TB_EINVAL
+                       fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, -1)), fake, fake, fake,
-                       fake, None, fake, 1 << 30, None) == tbl.TB_EINVAL
+                       fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, 1, n_sink=4)), fake,
-                       fake, fake, fake, None, fake, 1 << 30, None) == tbl.TB_EUNSUPPORTED
+                       fake, fake, fake, None, None, fake, 1 << 30, None) == tbl.TB_EUNSUPPORTED
     assert L.tb_project_keys(ctypes.byref(s), fake, fake, fake, -1, fake, None) == tbl.TB_EINVAL
     assert L.tb_project_keys(ctypes.byref(s), fake, fake, None, 4, fake, None) == tbl.TB_EINVAL
     # n_tokens == 0 is a no-op that launches nothing
     assert L.tb_project_keys(ctypes.byref(s), fake, fake, fake, 0, fake, None) == tbl.TB_OK
-    assert L.tb_sparse_attn(ctypes.byref(s), fake, fake, fake, fake, 0, fake, None, fake,
+    # lists without a stride, and neither lists nor a bitmap
+    assert L.tb_sparse_attn(ctypes.byref(s), fake, fake, fake, fake, 0, fake, None, None, fake,
+                            ctypes.c_float(0.1), fake, fake, 1 << 30, None) == tbl.TB_EINVAL
+    assert L.tb_sparse_attn(ctypes.byref(s), fake, fake, fake, None, 0, None, None, None, fake,
                             ctypes.c_float(0.1), fake, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_decode_step(ctypes.byref(s), ctypes.byref(p), None, fake, 1 << 30,
                             None) == tbl.TB_EINVAL
@@ -111,10 +116,10 @@ def test_workspace_checks():
     p = tbl.make_params(100, 1)
     need = tbl.workspace_bytes(s, p)
     fake = ctypes.c_void_p(1 << 20)
-    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, fake, fake, None, fake,
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, fake, fake, None, None, fake,
                        need - 1, None) == tbl.TB_EWORKSPACE
     misaligned = ctypes.c_void_p((1 << 20) + 8)
-    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, fake, fake, None,
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, fake, fake, None, None,
                        misaligned, need, None) == tbl.TB_EINVAL
 
 
@@ -126,7 +131,7 @@ def test_decode_step_argument_checks():
     fake = 1 << 20
     a = tbl.StepArgs()
     for f in ("q", "w", "k_cache", "v_cache", "kp_cache", "ctx_len", "sel_idx", "sel_count",
-              "keep_from", "out", "q_imp"):
+              "sel_bits", "keep_from", "out", "q_imp"):
         setattr(a, f, fake)
     a.n_new = 1          # new rows announced but not given
     a.refresh = 1
@@ -138,6 +143,10 @@ def test_decode_step_argument_checks():
     assert L.tb_decode_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(a),
                             ctypes.c_void_p(fake), need, None) == tbl.TB_EINVAL
     a.q_imp = fake
+    a.sel_bits = None    # the fused step keeps its selection as a bitmap
+    assert L.tb_decode_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(a),
+                            ctypes.c_void_p(fake), need, None) == tbl.TB_EINVAL
+    a.sel_bits = fake
     a.softmax_scale = float("nan")
     assert L.tb_decode_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(a),
                             ctypes.c_void_p(fake), need, None) == tbl.TB_EINVAL

@@ -15,8 +15,9 @@ from query_aware_kv_amd import synth
 from query_aware_kv_amd import tokenbutler as tbl
 from query_aware_kv_amd.workloads import (BATCHED_8K, INTERVAL_16K, LLAMA_32K, LONG_128K,
                                           TINY_F32, Workload)
-from tests.gpu_cases import (TOL, band_members, device_case, f64, lists_of, need_gpu, odtype,
-                             oracle_state, oracle_step, shape_of, step_on_device)
+from tests.gpu_cases import (TOL, band_members, bitmap_positions, device_case, f64, lists_of,
+                             need_gpu, odtype, oracle_state, oracle_step, shape_of,
+                             step_on_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,21 +73,27 @@ def test_stage_parity(w):
     assert np.all(np.abs(s32.astype(np.float64) - s64) <= np.abs(s64) * 2.0 ** -24 + 1e-300)
     # top-B and neighbor expansion: exact index sets
     topb = torch.full((w.batch, w.n_imp_heads, w.budget), -1, dtype=torch.int32, device="cuda")
-    tbl.select(dc.shape, dc.params, scores, ctx_len, dc.sel, dc.cnt, dc.ws, topb_idx=topb)
+    tbl.select(dc.shape, dc.params, scores, ctx_len, dc.sel, dc.cnt, dc.ws, topb_idx=topb,
+               sel_bits=dc.bits)
     torch.cuda.synchronize()
     got = lists_of(dc.sel, dc.cnt, b)
+    got_bits = bitmap_positions(dc.bits, b, ctx)
     S_ref = []
     for i in range(w.n_imp_heads):
         T_ref = orc.topb(s32[i], w.budget)
         assert topb[b, i, :T_ref.size].cpu().tolist() == T_ref.tolist(), i
         S_ref.append(orc.expand(T_ref, ctx, w.radius))
         assert got[i] == S_ref[-1].tolist(), i
+        assert got_bits[i] == S_ref[-1].tolist(), i
     # attention over S united with the appended token
     keep = torch.full((w.batch,), ctx - 1, dtype=torch.int32, device="cuda")
     q = synth.draw_q(w, 0)
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device="cuda")
+    out2 = torch.empty_like(out)
     tbl.sparse_attn(dc.shape, q.cuda(), dc.K, dc.V, dc.sel, dc.cap_s, dc.cnt, keep, ctx_len,
                     w.softmax_scale, out, dc.ws)
+    tbl.sparse_attn(dc.shape, q.cuda(), dc.K, dc.V, None, 0, None, keep, ctx_len,
+                    w.softmax_scale, out2, dc.ws, sel_bits=dc.bits)
     torch.cuda.synchronize()
     q64 = f64(q[b])
     err = 0.0
@@ -95,6 +102,8 @@ def test_stage_parity(w):
         ref = orc.attend(q64[h], K64[_kv(w, h)], V64[_kv(w, h)], A, w.softmax_scale)
         err = max(err, float(np.abs(f64(out[b, h]) - ref).max()))
     assert err <= TOL[w.dtype], err
+    # list and bitmap membership run the same arithmetic in the same order
+    assert torch.equal(out, out2)
 
 
 # --------------------------------------------------------------------------
@@ -215,7 +224,7 @@ def test_ragged_batch_fused(kw):
                          v_new=inp.v_new.cuda(), refresh=True, w=dc.W, k_cache=dc.K,
                          v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
                          softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
-                         keep_from=dc.keep, out=out)
+                         sel_bits=dc.bits, keep_from=dc.keep, out=out)
     tbl.decode_step(dc.shape, dc.params, args, dc.ws)
     torch.cuda.synchronize()
     for b, n in enumerate(lens):
@@ -247,15 +256,18 @@ def _select_case(scores_rows, lens, B, r):
     sel = torch.full((bsz, H, cap_s), -1, dtype=torch.int32, device="cuda")
     cnt = torch.full((bsz, H), -1, dtype=torch.int32, device="cuda")
     topb = torch.full((bsz, H, B), -1, dtype=torch.int32, device="cuda")
-    tbl.select(shape, params, sc, ctx, sel, cnt, ws, topb_idx=topb)
+    bits = torch.full((bsz, H, tbl.bitmap_words(shape)), -1, dtype=torch.int32, device="cuda")
+    tbl.select(shape, params, sc, ctx, sel, cnt, ws, topb_idx=topb, sel_bits=bits)
     torch.cuda.synchronize()
     for b in range(bsz):
         n = lens[b]
         got = lists_of(sel, cnt, b)
+        got_bits = bitmap_positions(bits, b, n)
         for i in range(H):
             T_ref = orc.topb(scores_rows[b, i, :n], B)
             assert topb[b, i, :T_ref.size].cpu().tolist() == T_ref.tolist(), (b, i)
             assert got[i] == orc.expand(T_ref, n, r).tolist(), (b, i)
+            assert got_bits[i] == got[i], (b, i)
 
 
 @pytest.mark.parametrize("B,r", [(1, 0), (5, 0), (37, 1), (100, 2), (700, 0), (64, 33)])
@@ -314,6 +326,12 @@ def test_empty_attended_set_gives_zero_rows():
                     w.softmax_scale, out, dc.ws)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out) == 0
+    dc.bits.zero_()
+    out.fill_(7.0)
+    tbl.sparse_attn(dc.shape, q, dc.K, dc.V, None, 0, None, None, ctx, w.softmax_scale, out,
+                    dc.ws, sel_bits=dc.bits)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
 
 
 def test_attention_ignores_list_entries_beyond_context():
@@ -345,6 +363,7 @@ def test_fused_step_is_deterministic():
         inp = synth.step_inputs(w, 0, dc.pre)
         out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
         step_on_device(dc, 0, inp, out)
-        outs.append((out.clone(), dc.sel.clone(), dc.cnt.clone(), dc.Kp.clone()))
+        outs.append((out.clone(), dc.sel.clone(), dc.cnt.clone(), dc.bits.clone(),
+                     dc.Kp.clone()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
