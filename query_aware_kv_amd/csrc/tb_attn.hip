@@ -17,8 +17,9 @@
 //   3. Rows stream through the lanes in 16-byte pieces (D*elt/16 lanes per
 //      row, several rows per wave, four rows in flight per row slot); each row
 //      slot keeps an online softmax (running max, sum, fp32 accumulator) per
-//      query head in base 2.  Dot products are reduced across the row's lanes
-//      with DPP row permutations.
+//      query head in base 2, rescaling only when the running max grows.  Lane
+//      dot products use v_dot2 on bf16 pairs and are reduced across the row's
+//      lanes with DPP row permutations.
 //   4. Row slots are merged by cross-lane shuffles, waves through LDS, into
 //      one partial (max, sum, acc[D]) per query head and chunk.
 //   5. The last work-group of a (sequence, KV head) to arrive (device-scope
@@ -33,7 +34,8 @@ namespace {
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kMaxChunks = kMaxCtxCap / kAttnChunk;
-constexpr int kRowsInFlight = 8; // rows per row slot loaded before use
+constexpr int kRowsInFlight = 4; // rows per row slot loaded before use
+constexpr int kMaxCounts = 1024;   // (mask group, position block, wave) ballot counts
 
 // Chunk partials cross work-groups (and XCDs, whose L2 caches are not
 // coherent with each other).  They are written and read with agent-scope
@@ -91,6 +93,30 @@ template <int N> __device__ __forceinline__ float group_sum(float x)
     return x;
 }
 
+// Dot product of the 16-byte q and k pieces held by one lane.
+__device__ __forceinline__ float lane_dot_bf16(const uint4 &q, const uint4 &k)
+{
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float d = 0.f;
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x),
+                                        __builtin_bit_cast(bf16x2, k.x), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y),
+                                        __builtin_bit_cast(bf16x2, k.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z),
+                                        __builtin_bit_cast(bf16x2, k.z), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w),
+                                        __builtin_bit_cast(bf16x2, k.w), d, false);
+    return d;
+}
+__device__ __forceinline__ float lane_dot_f32(const uint4 &q, const uint4 &k)
+{
+    float d = __uint_as_float(q.x) * __uint_as_float(k.x);
+    d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
+    d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
+    d = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+    return d;
+}
+
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *sel_idx;  // list mode
@@ -111,20 +137,28 @@ struct AttnArgs {
 template <typename T, int D, int GQ, bool BITMAP>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 {
+    auto lane_dot = [](const uint4 &qp, const uint4 &kp) -> float {
+        if constexpr (sizeof(T) == 2)
+            return lane_dot_bf16(qp, kp);
+        else
+            return lane_dot_f32(qp, kp);
+    };
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave step
     constexpr int NSLOT = kAttnWaves * RPW;  // row slots per work-group
     constexpr int NWD = kAttnChunk / 32;     // bitmap words per head
-    static_assert(NWD <= 64, "one wave compacts the union");
 
     __shared__ uint32_t bm[GQ][NWD];
     __shared__ uint32_t ulist[kAttnChunk];
+    __shared__ unsigned long long ubal[kMaxCounts];
+    __shared__ uint32_t uoff[kMaxCounts];
     __shared__ uint32_t s_misc[4];
     __shared__ float mrg_m[kAttnWaves][GQ];
     __shared__ float mrg_l[kAttnWaves][GQ];
     __shared__ float mrg_acc[kAttnWaves][GQ][D];
     __shared__ float cmb_f[GQ][kMaxChunks];
+    __shared__ float cmb_l[GQ][kMaxChunks];
     __shared__ float cmb_ml[GQ][2];
     __shared__ float4 red[kAttnThreads];
 
@@ -188,51 +222,88 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         __syncthreads();
 
         // ---- 2. union over the heads, compacted with head masks ----
-        if (wave == 0) {
-            uint32_t words[GQ];
-            uint32_t u = 0u;
+        // Every thread owns positions tid, tid + kAttnThreads, ... of the chunk.
+        // For 2 or 4 query heads per KV head the entries are ordered by head
+        // mask, then by position, so the row slots of one wave mostly share a
+        // mask and heads that no slot needs are skipped as a whole; otherwise
+        // they are ordered by position.  The order is deterministic: offsets
+        // come from per-wave ballots and one wave-wide scan.
+        {
+            constexpr int NIT = kAttnChunk / kAttnThreads;
+            constexpr int NGRP = (GQ == 2 || GQ == 4) ? (1 << GQ) - 1 : 1;
+            constexpr int NCNT = NGRP * NIT * kAttnWaves; // (group, it, wave), group-major
+            constexpr int PERL = (NCNT + 63) / 64;          // counts per lane of the scan
+            static_assert(NCNT <= kMaxCounts, "ballot table");
+            uint32_t tmask[NIT];
 #pragma unroll
-            for (int hl = 0; hl < GQ; ++hl) {
-                words[hl] = lane < NWD ? bm[hl][lane] : 0u;
-                u |= words[hl];
-            }
-            const uint32_t cnt = __popc(u);
-            uint32_t inc = cnt;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t v = __shfl_up(inc, off);
-                if (lane >= off)
-                    inc += v;
-            }
-            uint32_t pos = inc - cnt;
-            while (u) {
-                const int bit = __ffs(u) - 1;
-                uint32_t mask = 0u;
+            for (int it = 0; it < NIT; ++it) {
+                const int tl = it * kAttnThreads + tid;
+                uint32_t mk = 0u;
 #pragma unroll
                 for (int hl = 0; hl < GQ; ++hl)
-                    mask |= ((words[hl] >> bit) & 1u) << hl;
-                ulist[pos++] = (uint32_t)(lane * 32 + bit) | (mask << 16);
-                u &= u - 1u;
+                    mk |= ((bm[hl][tl >> 5] >> (tl & 31)) & 1u) << hl;
+                tmask[it] = mk;
             }
-            if (lane == 63)
-                s_misc[0] = inc;
+            auto group_of = [&](uint32_t mk) -> int { return NGRP == 1 ? 0 : (int)mk - 1; };
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+#pragma unroll
+                for (int gi = 0; gi < NGRP; ++gi) {
+                    const bool in = NGRP == 1 ? tmask[it] != 0u : tmask[it] == (uint32_t)(gi + 1);
+                    const unsigned long long bal = __ballot(in);
+                    if (lane == 0)
+                        ubal[(gi * NIT + it) * kAttnWaves + wave] = bal;
+                }
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // exclusive scan of the NCNT ballot counts, PERL per lane
+                uint32_t c[PERL], sum = 0u;
+#pragma unroll
+                for (int j = 0; j < PERL; ++j) {
+                    const int idx = lane * PERL + j;
+                    c[j] = idx < NCNT ? (uint32_t)__popcll(ubal[idx]) : 0u;
+                    sum += c[j];
+                }
+                uint32_t inc = sum;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t v = __shfl_up(inc, off);
+                    if (lane >= off)
+                        inc += v;
+                }
+                uint32_t run = inc - sum;
+#pragma unroll
+                for (int j = 0; j < PERL; ++j) {
+                    const int idx = lane * PERL + j;
+                    if (idx < NCNT)
+                        uoff[idx] = run;
+                    run += c[j];
+                }
+                if (lane == 63)
+                    s_misc[0] = inc;
+            }
+            __syncthreads();
+            const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                if (tmask[it] != 0u) {
+                    const int idx = (group_of(tmask[it]) * NIT + it) * kAttnWaves + wave;
+                    const uint32_t pos = uoff[idx] + (uint32_t)__popcll(ubal[idx] & below);
+                    ulist[pos] = (uint32_t)(it * kAttnThreads + tid) | (tmask[it] << 16);
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
 
         // ---- 3. stream the rows ----
         const int nu = (int)s_misc[0];
         const int slot = lane / LPR, sub = lane % LPR;
-        float qf[GQ][EPL];
+        // q slice of this lane, kept in the storage type (bf16 pairs feed v_dot2)
+        uint4 qv[GQ];
 #pragma unroll
-        for (int hl = 0; hl < GQ; ++hl) {
-            const uint4 piece =
-                *reinterpret_cast<const uint4 *>(q + (head0 + hl) * D + sub * EPL);
-            T v[EPL];
-            __builtin_memcpy(v, &piece, 16);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                qf[hl][e] = to_f32(v[e]) * a.qscale;
-        }
+        for (int hl = 0; hl < GQ; ++hl)
+            qv[hl] = *reinterpret_cast<const uint4 *>(q + (head0 + hl) * D + sub * EPL);
         float m[GQ], l[GQ], acc[GQ][EPL];
 #pragma unroll
         for (int hl = 0; hl < GQ; ++hl) {
@@ -246,31 +317,36 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         const T *kb = kc + kvbase * D + sub * EPL;
         const T *vb = vc + kvbase * D + sub * EPL;
 
+        // One row: for each query head that attends it, the logit (lane dot
+        // products reduced over the row's lanes), a running-max update that
+        // rescales only when the max grows, and the weighted V accumulation.
         auto consume = [&](uint32_t ent, const uint4 &kp, const uint4 &vp) {
-            T kv[EPL], vv[EPL];
-            __builtin_memcpy(kv, &kp, 16);
-            __builtin_memcpy(vv, &vp, 16);
             const uint32_t mask = ent >> 16;
-            float z[GQ];
-#pragma unroll
-            for (int hl = 0; hl < GQ; ++hl) {
-                float d = 0.f;
+            float vf[EPL];
+            {
+                T vv[EPL];
+                __builtin_memcpy(vv, &vp, 16);
 #pragma unroll
                 for (int e = 0; e < EPL; ++e)
-                    d = fmaf(qf[hl][e], to_f32(kv[e]), d);
-                z[hl] = group_sum<LPR>(d);
+                    vf[e] = to_f32(vv[e]);
             }
 #pragma unroll
             for (int hl = 0; hl < GQ; ++hl) {
                 if ((mask >> hl) & 1u) {
-                    const float mn = fmaxf(m[hl], z[hl]);
-                    const float corr = exp2f(m[hl] - mn);
-                    const float p = exp2f(z[hl] - mn);
-                    l[hl] = fmaf(l[hl], corr, p);
+                    const float z = group_sum<LPR>(lane_dot(qv[hl], kp)) * a.qscale;
+                    if (z > m[hl]) {
+                        const float corr = __builtin_amdgcn_exp2f(m[hl] - z);
+                        l[hl] *= corr;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            acc[hl][e] *= corr;
+                        m[hl] = z;
+                    }
+                    const float p = __builtin_amdgcn_exp2f(z - m[hl]);
+                    l[hl] += p;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e)
-                        acc[hl][e] = fmaf(acc[hl][e], corr, p * to_f32(vv[e]));
-                    m[hl] = mn;
+                        acc[hl][e] = fmaf(p, vf[e], acc[hl][e]);
                 }
             }
         };
@@ -278,26 +354,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             return (size_t)(c0 + (int)(ent & 0xffffu)) * D;
         };
 
-        // all of a slot's rows (up to kRowsInFlight) are requested before any is used
+        // All of a slot's rows (up to kRowsInFlight) are requested before any
+        // is used.  The loads are unconditional -- a missing row reads the
+        // chunk's first row, which always exists, and is then skipped -- so
+        // they issue back to back.
         for (int base = wave * RPW + slot; base < nu; base += kRowsInFlight * NSLOT) {
             uint32_t e[kRowsInFlight];
             uint4 kk[kRowsInFlight], vv[kRowsInFlight];
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
                 const int u = base + r * NSLOT;
-                e[r] = u < nu ? ulist[u] : 0xffffffffu;
+                e[r] = u < nu ? ulist[u] : 0u; // mask 0: nothing to do
             }
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
-                if (e[r] != 0xffffffffu) {
-                    kk[r] = *reinterpret_cast<const uint4 *>(kb + rowptr(e[r]));
-                    vv[r] = *reinterpret_cast<const uint4 *>(vb + rowptr(e[r]));
-                }
+                kk[r] = *reinterpret_cast<const uint4 *>(kb + rowptr(e[r]));
+                vv[r] = *reinterpret_cast<const uint4 *>(vb + rowptr(e[r]));
             }
+            // consume() runs for every row (a missing row has an empty head
+            // mask and skips every head), so no load is sunk into a branch
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r)
-                if (e[r] != 0xffffffffu)
-                    consume(e[r], kk[r], vv[r]);
+                consume(e[r], kk[r], vv[r]);
         }
 
         // ---- 4. merge row slots (shuffles) and waves (LDS) into the chunk partial ----
@@ -308,8 +386,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 const float mo = __shfl_xor(m[hl], off);
                 const float lo_ = __shfl_xor(l[hl], off);
                 const float mn = fmaxf(m[hl], mo);
-                const float fa = m[hl] == -INFINITY ? 0.f : exp2f(m[hl] - mn);
-                const float fb = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+                const float fa = m[hl] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hl] - mn);
+                const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
                 l[hl] = l[hl] * fa + lo_ * fb;
 #pragma unroll
                 for (int e = 0; e < EPL; ++e) {
@@ -344,7 +422,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 for (int s = 0; s < kAttnWaves; ++s) {
                     const float ms = mrg_m[s][hl];
                     if (ms != -INFINITY) {
-                        const float f = exp2f(ms - M);
+                        const float f = __builtin_amdgcn_exp2f(ms - M);
                         Ls = fmaf(mrg_l[s][hl], f, Ls);
                         O = fmaf(mrg_acc[s][hl][dim], f, O);
                     }
@@ -352,10 +430,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             }
             const size_t pc = (head0 + hl) * nchunk + c;
             store_agent(&a.part_o[pc * D + dim], O);
-            if (dim == 0) {
-                store_agent(&a.part_ml[pc * 2], M);
-                store_agent(&a.part_ml[pc * 2 + 1], Ls);
-            }
+            if (dim == 0)
+                __hip_atomic_store(reinterpret_cast<double *>(a.part_ml) + pc,
+                                   __builtin_bit_cast(double, make_float2(M, Ls)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
@@ -375,14 +453,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const int nact = (n + kAttnChunk - 1) / kAttnChunk;
-    // (a) chunk maxima and sums into LDS
+    // Every load of the merge is issued up front: the chunk (max, sum) pairs
+    // into LDS, and each thread's weighted-sum inputs into registers.
+    constexpr int NCOL = GQ * D / 4;
+    constexpr int NPART = kAttnThreads / NCOL;
+    static_assert(NPART >= 1 && NPART * NCOL == kAttnThreads, "column split");
+    constexpr int PER = kMaxChunks / NPART; // chunks per thread at most
+    const int col = tid % NCOL, part = tid / NCOL;
+    const int chl = col / (D / 4), d4 = col % (D / 4);
     for (int e = tid; e < GQ * nact; e += kAttnThreads) {
         const int hl = e / nact, cc = e % nact;
         const size_t pc = (head0 + hl) * nchunk + cc;
-        cmb_f[hl][cc] = load_agent(&a.part_ml[pc * 2]);
+        const double ml = __hip_atomic_load(reinterpret_cast<const double *>(a.part_ml) + pc,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float2 v = __builtin_bit_cast(float2, ml);
+        cmb_f[hl][cc] = v.x;
+        cmb_l[hl][cc] = v.y;
+    }
+    const float *po = a.part_o + (head0 + chl) * nchunk * D + d4 * 4;
+    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // chunk weights need the maxima; the first batch of partial sums is
+    // loaded meanwhile
+    constexpr int BATCH = 8;
+    float4 v0[BATCH];
+#pragma unroll
+    for (int r = 0; r < BATCH; ++r) {
+        const int cc = part + r * NPART;
+        v0[r] = load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
     }
     __syncthreads();
-    // (b) per head: global max, chunk weights, total sum (one wave per head)
     for (int hl = wave; hl < GQ; hl += kAttnWaves) {
         float M = -INFINITY;
         for (int cc = lane; cc < nact; cc += 64)
@@ -393,9 +492,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         float Ls = 0.f;
         for (int cc = lane; cc < nact; cc += 64) {
             const float mc = cmb_f[hl][cc];
-            const float f = (mc == -INFINITY) ? 0.f : exp2f(mc - M);
+            const float f = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
             cmb_f[hl][cc] = f;
-            Ls = fmaf(load_agent(&a.part_ml[((head0 + hl) * nchunk + cc) * 2 + 1]), f, Ls);
+            Ls = fmaf(cmb_l[hl][cc], f, Ls);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
@@ -404,42 +503,25 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             cmb_ml[hl][0] = Ls;
     }
     __syncthreads();
-    // (c) weighted sums: thread = (float4 column, chunk residue class)
-    constexpr int NCOL = GQ * D / 4;
-    constexpr int NPART = kAttnThreads / NCOL;
-    static_assert(NPART >= 1 && NPART * NCOL == kAttnThreads, "column split");
-    {
-        const int col = tid % NCOL, p = tid / NCOL;
-        const int hl = col / (D / 4), d4 = col % (D / 4);
-        const float *po = a.part_o + (head0 + hl) * nchunk * D + d4 * 4;
-        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-        int cc = p;
-        for (; cc + 3 * NPART < nact; cc += 4 * NPART) {
-            float4 v[4];
-            float f[4];
+    for (int c0b = part; c0b < nact; c0b += BATCH * NPART) {
+        float4 v[BATCH];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[r] = load4_agent(po + (size_t)(cc + r * NPART) * D);
-                f[r] = cmb_f[hl][cc + r * NPART];
-            }
+        for (int r = 0; r < BATCH; ++r) {
+            const int cc = c0b + r * NPART;
+            v[r] = c0b == part ? v0[r] : load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s.x = fmaf(v[r].x, f[r], s.x);
-                s.y = fmaf(v[r].y, f[r], s.y);
-                s.z = fmaf(v[r].z, f[r], s.z);
-                s.w = fmaf(v[r].w, f[r], s.w);
-            }
+        for (int r = 0; r < BATCH; ++r) {
+            const int cc = c0b + r * NPART;
+            const float f = cc < nact ? cmb_f[chl][cc] : 0.f;
+            s4.x = fmaf(v[r].x, f, s4.x);
+            s4.y = fmaf(v[r].y, f, s4.y);
+            s4.z = fmaf(v[r].z, f, s4.z);
+            s4.w = fmaf(v[r].w, f, s4.w);
         }
-        for (; cc < nact; cc += NPART) {
-            const float4 v = load4_agent(po + (size_t)cc * D);
-            const float f = cmb_f[hl][cc];
-            s.x = fmaf(v.x, f, s.x);
-            s.y = fmaf(v.y, f, s.y);
-            s.z = fmaf(v.z, f, s.z);
-            s.w = fmaf(v.w, f, s.w);
-        }
-        red[p * NCOL + col] = s;
     }
+    red[part * NCOL + col] = s4;
+    (void)PER;
     __syncthreads();
     T *out = (T *)a.out;
     for (int col = tid; col < NCOL; col += kAttnThreads) {
