@@ -45,9 +45,9 @@
  * - ctx_len[b] is the number of valid cache rows of sequence b; values are
  *   clamped to [0, ctx_cap] on the device.
  * - Arithmetic: projected keys are fp64 sums in ascending head_dim order,
- *   rounded once (to nearest even) to the dtype; scores are fp64 dot products
- *   in ascending d_imp order rounded once to fp32; attention accumulates in
- *   fp32.  Inputs must be finite.
+ *   rounded once (to nearest even) to the dtype; scores are fp32 fused
+ *   multiply-add chains in ascending d_imp order starting from +0; attention
+ *   accumulates in fp32.  Inputs must be finite.
  * - Return value: TB_OK, or a negative TB_E* code.  Every argument check runs
  *   on the host before anything is enqueued, so an error return means nothing
  *   was launched -- except TB_EHIP, which reports a failed launch.
@@ -132,8 +132,10 @@ int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
  * tb_score -- importance scores.  [ARCH]: each predicted importance query is
  * dotted with the projected keys of its KV head.
  *
- * scores[b][i][t] = fp32( sum_j q_imp[b][i][j] * kp_cache[b][g(i)][t][j] )
- * for t < ctx_len[b]; entries t >= ctx_len[b] are left untouched.
+ * scores[b][i][t] = acc_d, acc_0 = +0, acc_{j+1} = fmaf(q_imp[b][i][j],
+ * kp_cache[b][g(i)][t][j], acc_j) in fp32, for t < ctx_len[b]; entries
+ * t >= ctx_len[b] are left untouched.  The workspace is not used by this
+ * call but must still be given (it is checked like the others).
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,

@@ -97,8 +97,9 @@ def project(K, W, dtype: int) -> np.ndarray:
 def score(q_imp, Kp, n: int | None = None):
     """Scores of one sequence.  q_imp [Himp, d], Kp [Hkv, cap, d].
 
-    Returns (s64 [Himp, n], s32 [Himp, n]): the fp64 dot products and their
-    fp32 roundings, over tokens t < n (default: cap)."""
+    Returns (s64 [Himp, n], s32 [Himp, n]) over tokens t < n (default: cap):
+    the fp64 dot products, and the fp32 fused multiply-add chains (ascending
+    coordinate order) that decide the selection."""
     q_imp = _f64(q_imp)
     Kp = _f64(Kp)
     Himp, d = q_imp.shape

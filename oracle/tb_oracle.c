@@ -21,10 +21,12 @@
  *     bias ([ARCH] names a single learned matrix).
  *   - The projected key is the fp64 sum over the head dimension in ascending
  *     order, rounded once (round-to-nearest-even) to the cache dtype.
- *   - The importance score is the fp64 dot product of the importance query and
- *     the projected key in ascending order, rounded once to fp32.  The fp32
- *     value is the selection key ("the kernel's precision" for a decision that
- *     floating point makes).
+ *   - The importance score that decides the selection is computed in the
+ *     kernel's precision: an fp32 fused multiply-add chain over the d_imp
+ *     coordinates in ascending order, starting from +0.  (The pages fix no
+ *     precision; a floating-point result that decides an integer -- here the
+ *     kept set -- is taken in the same precision on both sides.)  The exact
+ *     fp64 dot product is reported beside it for accuracy checks.
  *   - Top-B orders tokens by (score descending, index ascending).  -0 and +0
  *     tie.  If B >= n every token is kept.
  *   - Neighbor fetching widens every kept token t to [t-r, t+r] clipped to
@@ -108,8 +110,12 @@ void orc_project(const double *K, const double *W, int64_t rows, int D, int d,
  * and Hkv KV heads (Himp is a multiple of Hkv). */
 static int imp_group(int i, int Himp, int Hkv) { return (int)((int64_t)i * Hkv / Himp); }
 
-/* For one sequence: s64[i][t] = sum_j q_imp[i][j] * Kp[g(i)][t][j] for t < n,
- * s32 = that value rounded to fp32.  Kp is [Hkv][cap][d]. */
+/* For one sequence and t < n (Kp is [Hkv][cap][d]):
+ *   s64[i][t] = sum_j q_imp[i][j] * Kp[g(i)][t][j] in fp64, ascending j;
+ *   s32[i][t] = the same sum as an fp32 fused multiply-add chain,
+ *               acc <- fmaf(q_imp[i][j], Kp[g(i)][t][j], acc), j ascending,
+ *               acc starting at +0.  The inputs are fp32/bf16 values, so
+ *               converting them to float is exact. */
 void orc_score(const double *q_imp, const double *Kp, int Himp, int Hkv, int cap,
                int d, int n, double *s64, float *s32)
 {
@@ -118,12 +124,15 @@ void orc_score(const double *q_imp, const double *Kp, int Himp, int Hkv, int cap
         for (int t = 0; t < n; ++t) {
             const double *k = Kp + ((int64_t)g * cap + t) * d;
             double acc = 0.0;
-            for (int j = 0; j < d; ++j)
+            float acc32 = 0.0f;
+            for (int j = 0; j < d; ++j) {
                 acc += q_imp[(int64_t)i * d + j] * k[j];
+                acc32 = fmaf((float)q_imp[(int64_t)i * d + j], (float)k[j], acc32);
+            }
             if (s64)
                 s64[(int64_t)i * n + t] = acc;
             if (s32)
-                s32[(int64_t)i * n + t] = (float)acc;
+                s32[(int64_t)i * n + t] = acc32;
         }
     }
 }

@@ -61,7 +61,6 @@ int32_t sel_capacity(const tb_shape &s, const tb_select_params &p)
 int hip_rc(hipError_t e) { return e == hipSuccess ? TB_OK : TB_EHIP; }
 
 struct Ws {
-    double *q64;
     float *scores;
     float *part_o;
     float *part_ml;
@@ -71,7 +70,7 @@ struct Ws {
 Ws carve(void *ws, const WsLayout &L)
 {
     char *base = (char *)ws;
-    return Ws{(double *)(base + L.qimp64), (float *)(base + L.scores),
+    return Ws{(float *)(base + L.scores),
               (float *)(base + L.part_o), (float *)(base + L.part_ml),
               (uint32_t *)(base + L.counters)};
 }
@@ -161,10 +160,9 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
-    Ws W = carve(ws, L);
-    hipStream_t st = (hipStream_t)stream;
-    TB_TRY(hip_rc(launch_qimp_f64(*shape, q_imp, W.q64, ctx_len, 0, nullptr, st)));
-    return hip_rc(launch_score(*shape, W.q64, kp_cache, ctx_len, scores, st));
+    return hip_rc(launch_score(*shape, q_imp, const_cast<void *>(kp_cache), ctx_len, scores, 0,
+                               nullptr, nullptr, nullptr, nullptr, nullptr,
+                               (hipStream_t)stream));
 }
 
 int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
@@ -179,7 +177,7 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
                                 sel_capacity(*shape, *params), sel_count, topb_idx, sel_bits,
-                                (hipStream_t)stream));
+                                nullptr, 0, (hipStream_t)stream));
 }
 
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
@@ -233,16 +231,20 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     hipStream_t st = (hipStream_t)stream;
     const int32_t stride = sel_capacity(*shape, *params);
 
-    if (a->n_new > 0)
+    // Refresh steps append inside the score launch when there are few new
+    // rows; otherwise (and on reuse steps) a separate launch appends them.
+    const bool fused_append = a->refresh && a->n_new > 0 && a->n_new <= score_max_fused_new();
+    if (a->n_new > 0 && !fused_append)
         TB_TRY(hip_rc(launch_append_project(*shape, a->k_new, a->v_new, a->n_new, a->w,
                                             a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
                                             st)));
     if (a->refresh) {
-        TB_TRY(hip_rc(launch_qimp_f64(*shape, a->q_imp, W.q64, a->ctx_len, a->n_new,
-                                      a->keep_from, st)));
-        TB_TRY(hip_rc(launch_score(*shape, W.q64, a->kp_cache, a->ctx_len, W.scores, st)));
+        TB_TRY(hip_rc(launch_score(*shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
+                                   fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
+                                   a->k_cache, a->v_cache, st)));
         TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
-                                    a->sel_count, nullptr, a->sel_bits, st)));
+                                    a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
+                                    st)));
     }
     return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
                               a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,

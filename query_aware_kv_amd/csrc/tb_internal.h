@@ -86,7 +86,6 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout (offsets in bytes from the workspace base).
 struct WsLayout {
-    size_t qimp64;   // fp64 copy of q_imp [b][Himp][d]
     size_t scores;   // fp32 scores [b][Himp][cap] (fused step only)
     size_t part_o;   // attention partial sums [b][Hq][nchunk][D] fp32
     size_t part_ml;  // attention partial (max, sum) [b][Hq][nchunk][2] fp32
@@ -101,8 +100,6 @@ inline WsLayout ws_layout(const tb_shape &s)
 {
     WsLayout L;
     size_t off = 0;
-    L.qimp64 = off;
-    off += align_up((size_t)s.batch * s.n_imp_heads * s.d_imp * sizeof(double));
     L.scores = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(float));
     L.part_o = off;
@@ -123,15 +120,20 @@ hipError_t launch_project(const tb_shape &s, const void *k_cache, const void *w,
 hipError_t launch_append_project(const tb_shape &s, const void *k_new, const void *v_new,
                                  int n_new, const void *w, void *k_cache, void *v_cache,
                                  void *kp_cache, const int32_t *ctx_len, hipStream_t st);
-hipError_t launch_qimp_f64(const tb_shape &s, const void *q_imp, double *q64,
-                           const int32_t *ctx_len, int n_new, int32_t *keep_from,
-                           hipStream_t st);
-hipError_t launch_score(const tb_shape &s, const double *q64, const void *kp_cache,
-                        const int32_t *ctx_len, float *scores, hipStream_t st);
+// Scores; when n_new > 0 (at most score_max_fused_new()) the same launch
+// appends the n_new rows of k_new / v_new at [ctx - n_new, ctx), projects
+// and scores them.
+int score_max_fused_new();
+hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
+                        const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
+                        const void *v_new, const void *w, void *k_cache, void *v_cache,
+                        hipStream_t st);
+// Selection; when keep_from is not NULL it also records
+// keep_from[b] = max(0, ctx_len[b] - n_new).
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
-                         hipStream_t st);
+                         int32_t *keep_from, int n_new, hipStream_t st);
 hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *sel_idx, int sel_stride,
                        const int32_t *sel_count, const uint32_t *sel_bits,

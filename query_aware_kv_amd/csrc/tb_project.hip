@@ -126,9 +126,9 @@ __global__ __launch_bounds__(256) void project_wide_kernel(
         T kv[RPT][EPC];
 #pragma unroll
         for (int rr = 0; rr < RPT; ++rr) {
-            uint4 piece = make_uint4(0, 0, 0, 0);
-            if (valid[rr])
-                piece = *reinterpret_cast<const uint4 *>(k_cache + rowoff[rr] * D + i0);
+            // unconditional (an invalid row reads row 0 and is not stored), so
+            // the loads issue back to back
+            const uint4 piece = *reinterpret_cast<const uint4 *>(k_cache + rowoff[rr] * D + i0);
             __builtin_memcpy(kv[rr], &piece, 16);
         }
 #pragma unroll
@@ -163,23 +163,6 @@ __global__ __launch_bounds__(256) void project_wide_kernel(
 #pragma unroll
         for (int p = 0; p < OPT * (int)sizeof(T) / 16; ++p)
             reinterpret_cast<uint4 *>(dst)[p] = reinterpret_cast<const uint4 *>(res)[p];
-    }
-}
-
-// q_imp -> fp64 copy, and (when keep_from != NULL) keep_from[b] = ctx - n_new.
-template <typename T>
-__global__ __launch_bounds__(256) void qimp_f64_kernel(const T *__restrict__ q_imp,
-                                                       double *__restrict__ q64, int count,
-                                                       const int32_t *__restrict__ ctx_len,
-                                                       int n_new, int batch, int cap,
-                                                       int32_t *__restrict__ keep_from)
-{
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (q_imp != nullptr && e < count)
-        q64[e] = to_f64(q_imp[e]);
-    if (keep_from != nullptr && e < batch) {
-        const int v = clamp_len(ctx_len[e], cap) - n_new;
-        keep_from[e] = v < 0 ? 0 : v;
     }
 }
 
@@ -250,24 +233,6 @@ hipError_t launch_append_project(const tb_shape &s, const void *k_new, const voi
         TB_DISPATCH_D_DI(append_dispatch_t, float, s, k_new, v_new, n_new, w, k_cache, v_cache,
                          kp_cache, ctx_len, st);
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_qimp_f64(const tb_shape &s, const void *q_imp, double *q64,
-                           const int32_t *ctx_len, int n_new, int32_t *keep_from,
-                           hipStream_t st)
-{
-    const int count = s.batch * s.n_imp_heads * s.d_imp;
-    const int work = count > s.batch ? count : s.batch;
-    const int grid = (work + 255) / 256;
-    if (s.dtype == TB_BF16)
-        hipLaunchKernelGGL(qimp_f64_kernel<bf16_t>, dim3(grid), dim3(256), 0, st,
-                           (const bf16_t *)q_imp, q64, count, ctx_len, n_new, s.batch, s.ctx_cap,
-                           keep_from);
-    else
-        hipLaunchKernelGGL(qimp_f64_kernel<float>, dim3(grid), dim3(256), 0, st,
-                           (const float *)q_imp, q64, count, ctx_len, n_new, s.batch, s.ctx_cap,
-                           keep_from);
-    return hipGetLastError();
 }
 
 } // namespace tb

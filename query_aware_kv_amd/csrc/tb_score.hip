@@ -1,45 +1,130 @@
-// tb_score.hip -- importance scores (gfx950).
+// tb_score.hip -- importance scores, with the append of new tokens folded in
+// (gfx950).
 //
 // TokenButler (gist.science technical summary, Methodology > Core
 // Architecture): each predicted low-dimensional importance query is dotted
 // with the projected keys of its KV head to score every cached token.
+// Inference Strategy > Optimizations: the projected-key cache is extended as
+// tokens arrive.
 //
 // One streaming pass over the projected-key cache: a lane owns one token of
 // one KV head, reads its d projected-key values (d*elt bytes, contiguous) in
-// 16-byte loads, widens them to fp64 once, and produces the scores of all
-// importance heads that read this KV head.  The importance queries of the
-// work-group are wave-uniform: they are read as fp64 through the scalar cache
-// (scalar loads into SGPRs), so each lane-token costs d fp64 fma per head.
+// 16-byte loads, and produces the scores of all importance heads that read
+// this KV head.  The importance queries are wave-uniform and come through the
+// scalar cache.
 //
-// Precision contract: score = fp32( sum_{j ascending} q[j] * kp[j] ) with the
-// sum in fp64.  Products of two bf16/fp32 values are exact in fp64, so the
-// fma chain equals the plain fp64 sum bit for bit; the one rounding to fp32
-// gives the selection key.
+// Precision contract: a score is the fp32 fused multiply-add chain over the
+// d coordinates in ascending order, starting from +0; this fp32 value is the
+// selection key.
+//
+// When the call also appends tokens, one extra work-group per (sequence, KV
+// head) -- the first one dispatched -- writes the new K/V rows into the
+// caches, projects their keys (fp64 sum in ascending head_dim order, rounded
+// once to the dtype) and scores them; the streaming work-groups skip those
+// positions, so no work-group waits for another.
 #include "tb_internal.h"
 
 namespace tb {
 namespace {
 
 constexpr int kScoreThreads = 256;
+constexpr int kMaxFusedNew = 8; // appended rows handled inside the score launch
+
+struct ScoreArgs {
+    const void *q_imp;  // [b][Himp][d]
+    void *kp;           // [b][Hkv][cap][d]
+    const int32_t *ctx_len;
+    float *scores;      // [b][Himp][cap]
+    int Himp, Hkv, cap;
+    // append (n_new == 0: none)
+    int n_new;
+    const void *k_new, *v_new; // [b][Hkv][n_new][D]
+    const void *w;             // [D][d]
+    void *k_cache, *v_cache;
+};
 
 template <typename T, int DI, int GI>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(
-    const double *__restrict__ q64, const T *__restrict__ kp, const int32_t *__restrict__ ctx_len,
-    int Himp, int Hkv, int cap, float *__restrict__ scores)
+__device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, int t,
+                                            const float (&k)[DI], bool valid)
 {
-    const int b = blockIdx.z;
-    const int g = blockIdx.y;
-    const int n = clamp_len(ctx_len[b], cap);
-    const int t0 = blockIdx.x * kScoreThreads;
-    if (t0 >= n)
+    const T *qb = (const T *)a.q_imp + ((size_t)b * a.Himp + (size_t)g * GI) * DI;
+    float *sb = a.scores + ((size_t)b * a.Himp + (size_t)g * GI) * a.cap;
+#pragma unroll
+    for (int hh = 0; hh < GI; ++hh) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < DI; ++j)
+            acc = fmaf(to_f32(qb[hh * DI + j]), k[j], acc);
+        if (valid)
+            sb[(size_t)hh * a.cap + t] = acc;
+    }
+}
+
+template <typename T, int D, int DI, int GI>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
+{
+    const int b = blockIdx.z, g = blockIdx.y;
+    const int n = clamp_len(a.ctx_len[b], a.cap);
+    const int nfresh = a.n_new < n ? a.n_new : n; // appended rows present in [0, n)
+    const int t_new = n - nfresh;                  // first appended position
+
+    // With appended rows, work-group 0 of each (b, g) is the append
+    // work-group (dispatched first, so its serial chain starts early) and the
+    // streaming tiles follow.
+    const bool has_append = a.n_new > 0;
+    if (has_append && blockIdx.x == 0) {
+        // ---- append work-group: copy, project and score the new rows ----
+        __shared__ float sW[D * DI];
+        __shared__ float sK[kMaxFusedNew][D];
+        if (nfresh == 0)
+            return;
+        const T *w = (const T *)a.w;
+        for (int e = threadIdx.x; e < D * DI; e += kScoreThreads)
+            sW[e] = to_f32(w[e]);
+        const size_t src0 = ((size_t)b * a.Hkv + g) * a.n_new + (a.n_new - nfresh);
+        const size_t dst0 = ((size_t)b * a.Hkv + g) * a.cap + t_new;
+        for (int e = threadIdx.x; e < nfresh * D; e += kScoreThreads) {
+            const int r = e / D, i = e % D;
+            const T kv = ((const T *)a.k_new)[(src0 + r) * D + i];
+            ((T *)a.k_cache)[(dst0 + r) * D + i] = kv;
+            ((T *)a.v_cache)[(dst0 + r) * D + i] = ((const T *)a.v_new)[(src0 + r) * D + i];
+            sK[r][i] = to_f32(kv);
+        }
+        __syncthreads();
+        __shared__ float sKp[kMaxFusedNew][DI];
+        for (int e = threadIdx.x; e < nfresh * DI; e += kScoreThreads) {
+            const int r = e / DI, j = e % DI;
+            double acc = 0.0;
+#pragma unroll 8
+            for (int i = 0; i < D; ++i)
+                acc = fma((double)sK[r][i], (double)sW[i * DI + j], acc);
+            const T kp = from_f64<T>(acc);
+            ((T *)a.kp)[(dst0 + r) * DI + j] = kp;
+            sKp[r][j] = to_f32(kp);
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < nfresh) {
+            float k[DI];
+#pragma unroll
+            for (int j = 0; j < DI; ++j)
+                k[j] = sKp[threadIdx.x][j];
+            score_heads<T, DI, GI>(a, b, g, t_new + threadIdx.x, k, true);
+        }
+        return;
+    }
+
+    // ---- streaming work-group: positions [t0, t0 + 256) below t_new ----
+    const int tile = (int)blockIdx.x - (has_append ? 1 : 0);
+    const int t0 = tile * kScoreThreads;
+    if (t0 >= t_new)
         return;
     const int t = t0 + threadIdx.x;
-    const bool valid = t < n;
+    const bool valid = t < t_new;
 
     constexpr int EPC = 16 / sizeof(T);
-    double k[DI];
+    float k[DI];
     {
-        const T *row = kp + (((size_t)b * Hkv + g) * cap + (valid ? t : t0)) * DI;
+        const T *row = (const T *)a.kp + (((size_t)b * a.Hkv + g) * a.cap + (valid ? t : t0)) * DI;
 #pragma unroll
         for (int p = 0; p < DI / EPC; ++p) {
             const uint4 piece = reinterpret_cast<const uint4 *>(row)[p];
@@ -47,59 +132,69 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(
             __builtin_memcpy(v, &piece, 16);
 #pragma unroll
             for (int e = 0; e < EPC; ++e)
-                k[p * EPC + e] = to_f64(v[e]);
+                k[p * EPC + e] = to_f32(v[e]);
         }
     }
-
-    const double *qb = q64 + ((size_t)b * Himp + (size_t)g * GI) * DI;
-    float *sb = scores + ((size_t)b * Himp + (size_t)g * GI) * cap;
-#pragma unroll
-    for (int hh = 0; hh < GI; ++hh) {
-        double acc = 0.0;
-#pragma unroll
-        for (int j = 0; j < DI; ++j)
-            acc = fma(qb[hh * DI + j], k[j], acc);
-        if (valid)
-            sb[(size_t)hh * cap + t] = (float)acc;
-    }
+    score_heads<T, DI, GI>(a, b, g, t, k, valid);
 }
 
-template <typename T, int DI, int GI>
-hipError_t score_t(const tb_shape &s, const double *q64, const void *kp, const int32_t *ctx_len,
-                   float *scores, hipStream_t st)
+template <typename T, int D, int DI, int GI>
+hipError_t score_t(const tb_shape &s, const ScoreArgs &a, hipStream_t st)
 {
-    dim3 grid((s.ctx_cap + kScoreThreads - 1) / kScoreThreads, s.n_kv_heads, s.batch);
-    hipLaunchKernelGGL((score_kernel<T, DI, GI>), grid, dim3(kScoreThreads), 0, st, q64,
-                       (const T *)kp, ctx_len, s.n_imp_heads, s.n_kv_heads, s.ctx_cap, scores);
+    const int ntiles = (s.ctx_cap + kScoreThreads - 1) / kScoreThreads;
+    dim3 grid(ntiles + (a.n_new > 0 ? 1 : 0), s.n_kv_heads, s.batch);
+    hipLaunchKernelGGL((score_kernel<T, D, DI, GI>), grid, dim3(kScoreThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename T, int DI>
-hipError_t score_gi(const tb_shape &s, const double *q64, const void *kp, const int32_t *ctx_len,
-                    float *scores, hipStream_t st)
+template <typename T, int D, int DI>
+hipError_t score_gi(const tb_shape &s, const ScoreArgs &a, hipStream_t st)
 {
     switch (s.n_imp_heads / s.n_kv_heads) {
-    case 1: return score_t<T, DI, 1>(s, q64, kp, ctx_len, scores, st);
-    case 2: return score_t<T, DI, 2>(s, q64, kp, ctx_len, scores, st);
-    case 4: return score_t<T, DI, 4>(s, q64, kp, ctx_len, scores, st);
-    case 8: return score_t<T, DI, 8>(s, q64, kp, ctx_len, scores, st);
+    case 1: return score_t<T, D, DI, 1>(s, a, st);
+    case 2: return score_t<T, D, DI, 2>(s, a, st);
+    case 4: return score_t<T, D, DI, 4>(s, a, st);
+    case 8: return score_t<T, D, DI, 8>(s, a, st);
     }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t score_dtype(const tb_shape &s, const ScoreArgs &a, hipStream_t st)
+{
+    if (s.head_dim == 64 && s.d_imp == 16) return score_gi<T, 64, 16>(s, a, st);
+    if (s.head_dim == 64 && s.d_imp == 32) return score_gi<T, 64, 32>(s, a, st);
+    if (s.head_dim == 128 && s.d_imp == 16) return score_gi<T, 128, 16>(s, a, st);
+    if (s.head_dim == 128 && s.d_imp == 32) return score_gi<T, 128, 32>(s, a, st);
     return hipErrorInvalidValue;
 }
 
 } // namespace
 
-hipError_t launch_score(const tb_shape &s, const double *q64, const void *kp_cache,
-                        const int32_t *ctx_len, float *scores, hipStream_t st)
+int score_max_fused_new() { return kMaxFusedNew; }
+
+hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
+                        const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
+                        const void *v_new, const void *w, void *k_cache, void *v_cache,
+                        hipStream_t st)
 {
-    if (s.dtype == TB_BF16) {
-        if (s.d_imp == 16) return score_gi<bf16_t, 16>(s, q64, kp_cache, ctx_len, scores, st);
-        if (s.d_imp == 32) return score_gi<bf16_t, 32>(s, q64, kp_cache, ctx_len, scores, st);
-    } else {
-        if (s.d_imp == 16) return score_gi<float, 16>(s, q64, kp_cache, ctx_len, scores, st);
-        if (s.d_imp == 32) return score_gi<float, 32>(s, q64, kp_cache, ctx_len, scores, st);
-    }
-    return hipErrorInvalidValue;
+    ScoreArgs a;
+    a.q_imp = q_imp;
+    a.kp = kp_cache;
+    a.ctx_len = ctx_len;
+    a.scores = scores;
+    a.Himp = s.n_imp_heads;
+    a.Hkv = s.n_kv_heads;
+    a.cap = s.ctx_cap;
+    a.n_new = n_new;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.w = w;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    if (s.dtype == TB_BF16)
+        return score_dtype<bf16_t>(s, a, st);
+    return score_dtype<float>(s, a, st);
 }
 
 } // namespace tb

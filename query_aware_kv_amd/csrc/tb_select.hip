@@ -6,8 +6,10 @@
 // fetching widens each kept token t to [t-r, t+r].
 //
 // One 1024-thread work-group per (sequence, importance head):
-//   1. Scores become order-preserving u32 keys (-0 folded onto +0).  Up to
-//      64 keys per thread stay in registers, so the scores are read once.
+//   1. Scores become order-preserving u32 keys (-0 folded onto +0).  Each
+//      thread owns whole 32-position words of the bitmap (word w = tid +
+//      j * 1024); up to two words (64 keys) per thread stay in registers, so
+//      the scores are read once, with 16-byte loads.
 //   2. Radix select from the top, 8 bits per pass, over the keys that match
 //      the prefix found so far.  Histograms live in LDS as 16 copies (lane
 //      mod 16), padded so that equal digits in different copies fall in
@@ -16,8 +18,8 @@
 //      When every key of that digit is needed the search stops early.
 //      Result: the threshold tau and how many keys equal to it are kept (the
 //      lowest positions first).
-//   3. A ballot pass writes the kept set T as an LDS bitmap; a block scan of
-//      per-word tie counts settles ties at tau by position.
+//   3. Every thread builds its own words of the kept set T from its keys; a
+//      block scan of per-word tie counts settles ties at tau by position.
 //   4. Dilation by r is word-wise shifts of the bitmap, clipped to [0, n).
 //   5. A block scan of per-word popcounts compacts the bitmap into the
 //      ascending index list; the bitmap itself can be written out too.
@@ -99,12 +101,45 @@ __device__ void compact_bits(const uint32_t *words, const uint32_t *offs, int nw
     }
 }
 
-template <int KPT>
+// Loads the 32 keys of bitmap word w (positions >= n become key 0, which is
+// below every real key and never counted).  Whole words of 16-byte aligned
+// rows use four-float loads; a partial last word, or a row whose start is
+// not 16-byte aligned, is read one float at a time without touching
+// positions >= n.
+__device__ __forceinline__ void load_word_keys(const float *row, int w, int n, bool vec,
+                                               uint32_t (&k)[32])
+{
+    const int p0 = w * 32;
+    if (vec && p0 + 32 <= n) {
+        const float4 *src = reinterpret_cast<const float4 *>(row + p0);
+        float4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            k[4 * i + 0] = score_key(v[i].x);
+            k[4 * i + 1] = score_key(v[i].y);
+            k[4 * i + 2] = score_key(v[i].z);
+            k[4 * i + 3] = score_key(v[i].w);
+        }
+    } else {
+        float f[32];
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            f[e] = row[p0 + e < n ? p0 + e : 0];
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            k[e] = p0 + e < n ? score_key(f[e]) : 0u;
+    }
+}
+
+template <int WPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
     int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
-    uint32_t *__restrict__ sel_bits, int bits_stride)
+    uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new)
 {
     extern __shared__ uint32_t lds[];
     uint32_t *hist = lds;                         // [kCopies][kCopyStride]
@@ -121,6 +156,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *row = scores + rowid * cap;
     const int n = clamp_len(ctx_len[b], cap);
     int32_t *out_sel = sel_idx + rowid * sel_stride;
+    if (keep_from != nullptr && i == 0 && tid == 0)
+        keep_from[b] = n - n_new > 0 ? n - n_new : 0;
     if (n == 0) {
         if (tid == 0)
             sel_count[rowid] = 0;
@@ -130,17 +167,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         return;
     }
     const int nw = (n + 31) >> 5;
-    const int nk = (n + kSelThreads - 1) / kSelThreads;
+    const int nwt = (nw + kSelThreads - 1) / kSelThreads; // words per thread (global mode)
+    const bool vec = (cap & 3) == 0; // every row starts 16-byte aligned
 
-    // keys[k] belongs to position k * kSelThreads + tid
-    constexpr int KR = KPT > 0 ? KPT : 1;
-    uint32_t keys[KR];
-    if constexpr (KPT > 0) {
+    // Keys of this thread: keys[j][bit] is position (tid + j * kSelThreads) * 32 + bit.
+    constexpr int WR = WPT > 0 ? WPT : 1;
+    uint32_t keys[WR][32];
+    if constexpr (WPT > 0) {
 #pragma unroll
-        for (int k = 0; k < KR; ++k) {
-            const int t = k * kSelThreads + tid;
-            keys[k] = t < n ? score_key(row[t]) : 0u;
-        }
+        for (int j = 0; j < WR; ++j)
+            load_word_keys(row, tid + j * kSelThreads, n, vec, keys[j]);
     }
 
     const bool take_all = B >= n;
@@ -153,22 +189,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         uint32_t *h = hist + (lane & (kCopies - 1)) * kCopyStride;
         for (int pass = 0; pass < 4; ++pass) {
             const int shift = 24 - 8 * pass;
-            if constexpr (KPT > 0) {
+            // key 0 marks a position >= n; real keys are never 0
+            auto count = [&](const uint32_t (&k)[32]) {
 #pragma unroll
-                for (int k = 0; k < KR; ++k) {
-                    const int t = k * kSelThreads + tid;
-                    const uint32_t key = keys[k];
-                    if (t < n && (key & pmask) == prefix)
-                        atomicAdd(&h[(key >> shift) & 255u], 1u);
-                }
+                for (int e = 0; e < 32; ++e)
+                    if (k[e] != 0u && (k[e] & pmask) == prefix)
+                        atomicAdd(&h[(k[e] >> shift) & 255u], 1u);
+            };
+            if constexpr (WPT > 0) {
+#pragma unroll
+                for (int j = 0; j < WR; ++j)
+                    count(keys[j]);
             } else {
-                for (int k = 0; k < nk; ++k) {
-                    const int t = k * kSelThreads + tid;
-                    if (t < n) {
-                        const uint32_t key = score_key(row[t]);
-                        if ((key & pmask) == prefix)
-                            atomicAdd(&h[(key >> shift) & 255u], 1u);
-                    }
+                for (int j = 0; j < nwt; ++j) {
+                    uint32_t k[32];
+                    load_word_keys(row, tid + j * kSelThreads, n, vec, k);
+                    count(k);
                 }
             }
             __syncthreads();
@@ -234,32 +270,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const bool partial_ties = !take_all && need < cnt_eq;
 
     // ---- kept-set bitmap (and tie bitmap when ties are split) ----
-    auto emit = [&](int k, uint32_t key) {
-        const int t = k * kSelThreads + tid;
-        const bool valid = t < n;
-        const uint32_t km = key & fmask;
-        const bool gt = valid && (take_all || km > tau || (!partial_ties && km == tau));
-        const bool eq = valid && partial_ties && km == tau;
-        const unsigned long long mg = __ballot(gt);
-        const unsigned long long me = __ballot(eq);
-        const int w0 = (k * kSelThreads + wave * 64) >> 5;
-        if (lane == 0 && w0 < nw) {
-            Tb[w0] = (uint32_t)mg;
-            Sb[w0] = (uint32_t)me;
-        }
-        if (lane == 0 && w0 + 1 < nw) {
-            Tb[w0 + 1] = (uint32_t)(mg >> 32);
-            Sb[w0 + 1] = (uint32_t)(me >> 32);
-        }
-    };
-    if constexpr (KPT > 0) {
+    auto emit = [&](int w, const uint32_t (&k)[32]) {
+        if (w >= nw)
+            return;
+        uint32_t gt = 0u, eq = 0u;
 #pragma unroll
-        for (int k = 0; k < KR; ++k)
-            emit(k, keys[k]);
+        for (int e = 0; e < 32; ++e) {
+            const uint32_t km = k[e] & fmask;
+            const bool valid = k[e] != 0u;
+            const bool in = valid && (take_all || km > tau || (!partial_ties && km == tau));
+            const bool tie = valid && partial_ties && km == tau;
+            gt |= (uint32_t)in << e;
+            eq |= (uint32_t)tie << e;
+        }
+        Tb[w] = gt;
+        Sb[w] = eq;
+    };
+    if constexpr (WPT > 0) {
+#pragma unroll
+        for (int j = 0; j < WR; ++j)
+            emit(tid + j * kSelThreads, keys[j]);
     } else {
-        for (int k = 0; k < nk; ++k) {
-            const int t = k * kSelThreads + tid;
-            emit(k, t < n ? score_key(row[t]) : 0u);
+        for (int j = 0; j < nwt; ++j) {
+            uint32_t k[32];
+            load_word_keys(row, tid + j * kSelThreads, n, vec, k);
+            emit(tid + j * kSelThreads, k);
         }
     }
     __syncthreads();
@@ -325,24 +360,26 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         sel_count[rowid] = (int32_t)total;
 }
 
-template <int KPT>
+template <int WPT>
 hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
-                    int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits, hipStream_t st)
+                    int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
+                    int32_t *keep_from, int n_new, hipStream_t st)
 {
     const int nwc = (s.ctx_cap + 31) / 32 + 1;
     const size_t lds =
         ((size_t)kCopies * kCopyStride + 256 + 64 + 4 * (size_t)nwc) * sizeof(uint32_t);
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<KPT>,
+        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<WPT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
     }
     dim3 grid(s.n_imp_heads, s.batch);
-    hipLaunchKernelGGL(select_kernel<KPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
+    hipLaunchKernelGGL(select_kernel<WPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
                        s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx, sel_stride,
-                       sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap));
+                       sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap), keep_from,
+                       n_new);
     return hipGetLastError();
 }
 
@@ -351,17 +388,13 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
-                         hipStream_t st)
+                         int32_t *keep_from, int n_new, hipStream_t st)
 {
-#define TB_SEL_ARGS s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, st
-    const int per = (s.ctx_cap + kSelThreads - 1) / kSelThreads;
-    if (per <= 1) return select_t<1>(TB_SEL_ARGS);
-    if (per <= 2) return select_t<2>(TB_SEL_ARGS);
-    if (per <= 4) return select_t<4>(TB_SEL_ARGS);
-    if (per <= 8) return select_t<8>(TB_SEL_ARGS);
-    if (per <= 16) return select_t<16>(TB_SEL_ARGS);
-    if (per <= 32) return select_t<32>(TB_SEL_ARGS);
-    if (per <= 64) return select_t<64>(TB_SEL_ARGS);
+#define TB_SEL_ARGS                                                                          \
+    s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from, n_new, st
+    const int words = (s.ctx_cap + 31) / 32;
+    if (words <= kSelThreads) return select_t<1>(TB_SEL_ARGS);
+    if (words <= 2 * kSelThreads) return select_t<2>(TB_SEL_ARGS);
     return select_t<0>(TB_SEL_ARGS);
 #undef TB_SEL_ARGS
 }

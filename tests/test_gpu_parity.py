@@ -69,8 +69,13 @@ def test_stage_parity(w):
     tbl.score(dc.shape, qi, dc.Kp, ctx_len, scores, dc.ws)
     s64, s32 = orc.score(f64(pre.q_imp0[b]), Kp_ref, n=ctx)
     np.testing.assert_array_equal(scores[b, :, :ctx].cpu().numpy(), s32)
-    # the fp32 scores are within the fp64 rounding of the exact dot products
-    assert np.all(np.abs(s32.astype(np.float64) - s64) <= np.abs(s64) * 2.0 ** -24 + 1e-300)
+    # the fp32 fma chains stay within the a-priori bound d * 2^-24 * sum |q_j kp_j|
+    # of the fp64 dot products
+    qa = np.abs(f64(pre.q_imp0[b]))
+    for i in range(w.n_imp_heads):
+        g = i * w.n_kv_heads // w.n_imp_heads
+        bound = w.d_imp * 2.0 ** -24 * (np.abs(Kp_ref[g, :ctx]) @ qa[i])
+        assert np.all(np.abs(s32[i].astype(np.float64) - s64[i]) <= bound + 1e-30), i
     # top-B and neighbor expansion: exact index sets
     topb = torch.full((w.batch, w.n_imp_heads, w.budget), -1, dtype=torch.int32, device="cuda")
     tbl.select(dc.shape, dc.params, scores, ctx_len, dc.sel, dc.cnt, dc.ws, topb_idx=topb,

@@ -160,7 +160,7 @@ def test_score_head_to_group_mapping_is_contiguous_blocks():
     assert s64[:, 0].tolist() == [1, 1, 1, 1, 2, 2, 2, 2]
 
 
-def test_score_against_integer_matmul_and_fp32_rounding():
+def test_score_against_integer_matmul():
     rng = np.random.default_rng(7)
     Hkv, cap, d = 4, 33, 8
     Kp = rng.integers(-50, 51, size=(Hkv, cap, d)).astype(np.float64)
@@ -170,11 +170,56 @@ def test_score_against_integer_matmul_and_fp32_rounding():
         g = i // 2
         ref = (Kp[g, :30].astype(np.int64) @ q_imp[i].astype(np.int64)).astype(np.float64)
         np.testing.assert_array_equal(s64[i], ref)
-    # fp32 rounding of a value that is not representable
-    q = np.array([[1.0, 2.0 ** -30]])
-    Kp1 = np.array([[[1.0, 1.0]]])
-    s64, s32 = orc.score(q, Kp1)
-    assert s64[0, 0] == 1.0 + 2.0 ** -30 and s32[0, 0] == np.float32(1.0)
+        np.testing.assert_array_equal(s32[i].astype(np.float64), ref)  # small integers: exact
+
+
+def _fma_chain_exact(q, k):
+    """Brute force of an fp32 fused multiply-add chain: each step rounds the
+    exact rational q_j * k_j + acc to the nearest fp32 (ties to even) -- done
+    here through Fraction arithmetic and a correctly rounded conversion."""
+    acc = Fraction(0)
+    for qj, kj in zip(q, k):
+        exact = Fraction(float(qj)) * Fraction(float(kj)) + acc
+        acc = Fraction(float(np.float32(_round_fraction_to_f32(exact))))
+    return float(acc)
+
+
+def _round_fraction_to_f32(x: Fraction) -> float:
+    # nearest fp32 to a rational, ties to even, by exact comparison of neighbours
+    if x == 0:
+        return 0.0
+    sign = -1.0 if x < 0 else 1.0
+    ax = abs(x)
+    f = float(ax)                     # correctly rounded to double
+    c = np.float32(f)                 # candidate near the answer
+    cands = {float(c), float(np.nextafter(c, np.float32(0))), float(np.nextafter(c, np.float32(np.inf)))}
+    best = min(cands, key=lambda v: (abs(Fraction(v) - ax),
+                                     int(np.float32(v).view(np.uint32)) & 1))
+    return sign * best
+
+
+def test_score_fp32_fma_chain_brute_force():
+    # the selection score is the fp32 fma chain; checked against exact
+    # rational arithmetic rounded at every step, on fp32 inputs where a
+    # separate multiply and add would differ
+    rng = np.random.default_rng(8)
+    d = 16
+    for trial in range(200):
+        q = rng.standard_normal(d).astype(np.float32)
+        k = rng.standard_normal((1, 1, d)).astype(np.float32)
+        _, s32 = orc.score(q[None, :].astype(np.float64), k.astype(np.float64))
+        assert float(s32[0, 0]) == _fma_chain_exact(q, k[0, 0]), trial
+
+
+def test_score_fp32_chain_is_ordered():
+    # ascending order matters: a large cancellation early keeps a small term
+    q = np.array([[1.0, 1.0, 1.0]])
+    kp = np.array([[[2.0 ** 30, -(2.0 ** 30), 1.0]]])
+    _, s32 = orc.score(q, kp)
+    assert s32[0, 0] == 1.0
+    kp = np.array([[[2.0 ** 30, 1.0, -(2.0 ** 30)]]])   # 2^30 + 1 rounds to 2^30 in fp32
+    _, s32 = orc.score(q, kp)
+    assert s32[0, 0] == 0.0
 
 
 # --------------------------------------------------------------------------
