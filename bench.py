@@ -34,6 +34,7 @@ from query_aware_kv_amd import tokenbutler as tbl  # noqa: E402
 from query_aware_kv_amd.workloads import LLAMA_32K  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_llama3_8b_ctx32k_traffic.json")
 METRIC = "sparse decode steps/sec at 32K ctx (Llama-3-8B shape); achieved HBM GB/s vs peak"
 
 
@@ -60,6 +61,27 @@ def unique_rows(sel, cnt, w, ctx: int) -> tuple[int, int]:
             rows |= lst
         uniq += len(rows)
     return uniq, logical
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
+    a plain copy of known size), or None when the kernel sources changed
+    after the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        h = hashlib.sha256()
+        for rel in t["source_files"]:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != t["source_sha256"]:
+            return None
+        return (t["fetch_kib_per_dispatch"] * t["fetch_scale"]
+                + t["write_kib_per_dispatch"] * t["write_scale"]) * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, pre, inp, seconds: float, max_steps: int) -> dict:
@@ -213,7 +235,7 @@ def main() -> int:
                    "storage": w.dtype, "replicas": R},
         "roofline": {"bound": "hbm", "kernel": "attn_kernel (tb_sparse_attn)",
                      "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "frac": attn_gbs / PEAK_HBM_GBS, "traffic": measured_traffic(),
                      "algorithmic_bytes": gather_bytes, "us_per_launch": ms_attn * 1e3},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
                      "frac": step_gbs / PEAK_HBM_GBS, "unique_rows": uniq,

@@ -35,7 +35,7 @@ struct ScoreArgs {
     void *kp;           // [b][Hkv][cap][d]
     const int32_t *ctx_len;
     float *scores;      // [b][Himp][cap]
-    int Himp, Hkv, cap;
+    int Himp, Hkv, cap, batch, ntiles;
     // append (n_new == 0: none)
     int n_new;
     const void *k_new, *v_new; // [b][Hkv][n_new][D]
@@ -63,16 +63,21 @@ __device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, in
 template <typename T, int D, int DI, int GI>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
 {
-    const int b = blockIdx.z, g = blockIdx.y;
+    // 1-D grid.  With appended rows the first batch*Hkv work-groups (the
+    // first dispatched, so their serial chains start early) are the append
+    // work-groups of each (b, g); the streaming tiles follow, tile-fastest.
+    const int napp = a.n_new > 0 ? a.batch * a.Hkv : 0;
+    const int id = blockIdx.x;
+    const bool is_append = id < napp;
+    const int sid = is_append ? id : id - napp;
+    const int bg = is_append ? sid : sid / a.ntiles;
+    const int tile = is_append ? 0 : sid % a.ntiles;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int n = clamp_len(a.ctx_len[b], a.cap);
     const int nfresh = a.n_new < n ? a.n_new : n; // appended rows present in [0, n)
     const int t_new = n - nfresh;                  // first appended position
 
-    // With appended rows, work-group 0 of each (b, g) is the append
-    // work-group (dispatched first, so its serial chain starts early) and the
-    // streaming tiles follow.
-    const bool has_append = a.n_new > 0;
-    if (has_append && blockIdx.x == 0) {
+    if (is_append) {
         // ---- append work-group: copy, project and score the new rows ----
         __shared__ float sW[D * DI];
         __shared__ float sK[kMaxFusedNew][D];
@@ -114,7 +119,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
     }
 
     // ---- streaming work-group: positions [t0, t0 + 256) below t_new ----
-    const int tile = (int)blockIdx.x - (has_append ? 1 : 0);
     const int t0 = tile * kScoreThreads;
     if (t0 >= t_new)
         return;
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
 template <typename T, int D, int DI, int GI>
 hipError_t score_t(const tb_shape &s, const ScoreArgs &a, hipStream_t st)
 {
-    const int ntiles = (s.ctx_cap + kScoreThreads - 1) / kScoreThreads;
-    dim3 grid(ntiles + (a.n_new > 0 ? 1 : 0), s.n_kv_heads, s.batch);
+    const int bg = s.batch * s.n_kv_heads;
+    dim3 grid((a.n_new > 0 ? bg : 0) + a.ntiles * bg);
     hipLaunchKernelGGL((score_kernel<T, D, DI, GI>), grid, dim3(kScoreThreads), 0, st, a);
     return hipGetLastError();
 }
@@ -186,6 +190,8 @@ hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
     a.Himp = s.n_imp_heads;
     a.Hkv = s.n_kv_heads;
     a.cap = s.ctx_cap;
+    a.batch = s.batch;
+    a.ntiles = (s.ctx_cap + kScoreThreads - 1) / kScoreThreads;
     a.n_new = n_new;
     a.k_new = k_new;
     a.v_new = v_new;
