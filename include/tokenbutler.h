@@ -48,6 +48,8 @@
  *   rounded once (to nearest even) to the dtype; scores are fp32 fused
  *   multiply-add chains in ascending d_imp order starting from +0; attention
  *   accumulates in fp32.  Inputs must be finite.
+ * - Alignment: tensors read or written in 16-byte pieces (K/V/Kp caches, q,
+ *   W, k_new, v_new) must be 16-byte aligned, else TB_EINVAL.
  * - Return value: TB_OK, or a negative TB_E* code.  Every argument check runs
  *   on the host before anything is enqueued, so an error return means nothing
  *   was launched -- except TB_EHIP, which reports a failed launch.

@@ -140,7 +140,7 @@ int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
     if (k_cache == nullptr || w == nullptr || pos0 == nullptr || kp_cache == nullptr ||
         n_tokens < 0)
         return TB_EINVAL;
-    if (!aligned16(k_cache) || !aligned16(kp_cache))
+    if (!aligned16(k_cache) || !aligned16(kp_cache) || !aligned16(w))
         return TB_EINVAL;
     if (n_tokens == 0)
         return TB_OK;
@@ -221,7 +221,8 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     if (a->refresh && a->q_imp == nullptr)
         return TB_EINVAL;
     if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
-        !aligned16(a->kp_cache))
+        !aligned16(a->kp_cache) || !aligned16(a->w) || !aligned16(a->k_new) ||
+        !aligned16(a->v_new))
         return TB_EINVAL;
     if (!(a->softmax_scale == a->softmax_scale))
         return TB_EINVAL;

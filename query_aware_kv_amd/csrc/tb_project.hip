@@ -19,6 +19,33 @@
 namespace tb {
 namespace {
 
+// W [D][DI] into LDS as fp64, read in 16-byte pieces that are all requested
+// before any is used (256 threads).
+template <typename T, int D, int DI>
+__device__ __forceinline__ void stage_w_f64(const T *__restrict__ w, double *sW)
+{
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int WP = D * DI / EPC;
+    constexpr int WPT = (WP + 255) / 256;
+    uint4 wp[WPT];
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+        const int pi = threadIdx.x + q * 256;
+        wp[q] = reinterpret_cast<const uint4 *>(w)[pi < WP ? pi : 0];
+    }
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+        const int pi = threadIdx.x + q * 256;
+        if (pi < WP) {
+            T v[EPC];
+            __builtin_memcpy(v, &wp[q], 16);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                sW[pi * EPC + e] = to_f64(v[e]);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Few rows (the per-step append): one thread per (row, output column).  The
 // W matrix and the work-group's K rows are staged in LDS as fp64.
@@ -33,8 +60,7 @@ __global__ __launch_bounds__(256) void project_rows_kernel(
     __shared__ double sW[D * DI];
     __shared__ double sK[ROWS][D + 1];
 
-    for (int e = threadIdx.x; e < D * DI; e += 256)
-        sW[e] = to_f64(w[e]);
+    stage_w_f64<T, D, DI>(w, sW);
 
     const int rl = threadIdx.x / DI;
     const int j = threadIdx.x % DI;
@@ -91,8 +117,7 @@ __global__ __launch_bounds__(256) void project_wide_kernel(
     constexpr int EPC = 16 / sizeof(T); // elements per 16-byte piece
     __shared__ double sW[D * DI];
 
-    for (int e = threadIdx.x; e < D * DI; e += 256)
-        sW[e] = to_f64(w[e]);
+    stage_w_f64<T, D, DI>(w, sW);
     __syncthreads();
 
     const int js = threadIdx.x % JS;

@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kScoreThreads = 256;
 constexpr int kMaxFusedNew = 8; // appended rows handled inside the score launch
+static_assert(kMaxFusedNew * 32 <= kScoreThreads, "one 16-byte piece of a new row per thread");
 
 struct ScoreArgs {
     const void *q_imp;  // [b][Himp][d]
@@ -83,17 +84,45 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
         __shared__ float sK[kMaxFusedNew][D];
         if (nfresh == 0)
             return;
-        const T *w = (const T *)a.w;
-        for (int e = threadIdx.x; e < D * DI; e += kScoreThreads)
-            sW[e] = to_f32(w[e]);
+        // W and the new K rows arrive in 16-byte pieces, all loads issued
+        // before any is used
+        constexpr int EPC = 16 / sizeof(T);
+        constexpr int WP = D * DI / EPC; // pieces of W
+        constexpr int WPT = (WP + kScoreThreads - 1) / kScoreThreads;
+        uint4 wp[WPT];
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int pi = threadIdx.x + q * kScoreThreads;
+            wp[q] = reinterpret_cast<const uint4 *>(a.w)[pi < WP ? pi : 0];
+        }
         const size_t src0 = ((size_t)b * a.Hkv + g) * a.n_new + (a.n_new - nfresh);
         const size_t dst0 = ((size_t)b * a.Hkv + g) * a.cap + t_new;
-        for (int e = threadIdx.x; e < nfresh * D; e += kScoreThreads) {
-            const int r = e / D, i = e % D;
-            const T kv = ((const T *)a.k_new)[(src0 + r) * D + i];
-            ((T *)a.k_cache)[(dst0 + r) * D + i] = kv;
-            ((T *)a.v_cache)[(dst0 + r) * D + i] = ((const T *)a.v_new)[(src0 + r) * D + i];
-            sK[r][i] = to_f32(kv);
+        constexpr int RP = D / EPC; // pieces per row
+        const int npc = nfresh * RP;
+        uint4 kpc = make_uint4(0, 0, 0, 0), vpc = make_uint4(0, 0, 0, 0);
+        const int e0 = threadIdx.x < npc ? (int)threadIdx.x : 0;
+        kpc = reinterpret_cast<const uint4 *>((const T *)a.k_new + src0 * D)[e0];
+        vpc = reinterpret_cast<const uint4 *>((const T *)a.v_new + src0 * D)[e0];
+#pragma unroll
+        for (int q = 0; q < WPT; ++q) {
+            const int pi = threadIdx.x + q * kScoreThreads;
+            if (pi < WP) {
+                T v[EPC];
+                __builtin_memcpy(v, &wp[q], 16);
+#pragma unroll
+                for (int e = 0; e < EPC; ++e)
+                    sW[pi * EPC + e] = to_f32(v[e]);
+            }
+        }
+        if ((int)threadIdx.x < npc) {
+            const int r = threadIdx.x / RP, i0 = (threadIdx.x % RP) * EPC;
+            reinterpret_cast<uint4 *>((T *)a.k_cache + (dst0 + r) * D)[threadIdx.x % RP] = kpc;
+            reinterpret_cast<uint4 *>((T *)a.v_cache + (dst0 + r) * D)[threadIdx.x % RP] = vpc;
+            T v[EPC];
+            __builtin_memcpy(v, &kpc, 16);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                sK[r][i0 + e] = to_f32(v[e]);
         }
         __syncthreads();
         __shared__ float sKp[kMaxFusedNew][DI];
@@ -108,12 +137,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
             sKp[r][j] = to_f32(kp);
         }
         __syncthreads();
-        if ((int)threadIdx.x < nfresh) {
-            float k[DI];
+        if ((int)threadIdx.x < nfresh * GI) {
+            // one thread per (new row, importance head)
+            const int r = threadIdx.x / GI, hh = threadIdx.x % GI;
+            const T *qh = (const T *)a.q_imp + ((size_t)b * a.Himp + (size_t)g * GI + hh) * DI;
+            float acc = 0.f;
 #pragma unroll
             for (int j = 0; j < DI; ++j)
-                k[j] = sKp[threadIdx.x][j];
-            score_heads<T, DI, GI>(a, b, g, t_new + threadIdx.x, k, true);
+                acc = fmaf(to_f32(qh[j]), sKp[r][j], acc);
+            a.scores[((size_t)b * a.Himp + (size_t)g * GI + hh) * a.cap + t_new + r] = acc;
         }
         return;
     }
