@@ -42,24 +42,20 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def unique_rows(sel, cnt, w, ctx: int) -> tuple[int, int]:
+def unique_rows(bits, w, ctx: int) -> tuple[int, int]:
     """(unique K/V rows over the KV groups, logical rows over the query heads)
-    of one sequence, counted from the library's own index output; the always
-    kept appended token is included."""
-    s = sel[0].cpu().numpy()
-    c = cnt[0].cpu().numpy()
+    of one sequence, counted from the library's own selection bitmap; the
+    always kept appended token is included."""
+    words = bits[0].cpu().numpy().astype(np.uint32)
+    members = np.unpackbits(words.view(np.uint8), axis=-1, bitorder="little")[:, :ctx]
+    members[:, ctx - 1] = 1
+    G = w.n_q_heads // w.n_kv_heads
     uniq = 0
     logical = 0
-    G = w.n_q_heads // w.n_kv_heads
     for g in range(w.n_kv_heads):
-        rows = {ctx - 1}
-        for h in range(g * G, (g + 1) * G):
-            i = h * w.n_imp_heads // w.n_q_heads
-            lst = set(s[i, :c[i]].tolist())
-            lst.add(ctx - 1)
-            logical += len(lst)
-            rows |= lst
-        uniq += len(rows)
+        heads = [h * w.n_imp_heads // w.n_q_heads for h in range(g * G, (g + 1) * G)]
+        logical += int(members[heads].sum())
+        uniq += int(members[sorted(set(heads))].any(axis=0).sum())
     return uniq, logical
 
 
@@ -134,7 +130,6 @@ def main() -> int:
     shape = tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
                            w.d_imp, w.ctx_cap, synth.torch_dtype(w))
     params = tbl.make_params(w.budget, w.radius)
-    cap_s = tbl.selection_capacity(shape, params)
 
     K0, V0, W = pre.K.to(dev), pre.V.to(dev), pre.W.to(dev)
     Kp0 = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=K0.dtype, device=dev)
@@ -144,7 +139,6 @@ def main() -> int:
     for r in range(a.replicas):
         reps.append(dict(
             K=K0.clone(), V=V0.clone(), Kp=Kp0.clone(),
-            sel=torch.zeros((w.batch, w.n_imp_heads, cap_s), dtype=torch.int32, device=dev),
             cnt=torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev),
             bits=torch.zeros((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)),
                              dtype=torch.int32, device=dev),
@@ -157,7 +151,7 @@ def main() -> int:
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device=dev)
     step_args = [tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=True, w=W,
                                k_cache=r["K"], v_cache=r["V"], kp_cache=r["Kp"], ctx_len=ctx,
-                               softmax_scale=w.softmax_scale, sel_idx=r["sel"],
+                               softmax_scale=w.softmax_scale, sel_idx=None,
                                sel_count=r["cnt"], sel_bits=r["bits"], keep_from=r["keep"],
                                out=out)
                  for r in reps]
@@ -193,7 +187,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_attn = e0.elapsed_time(e1) / a.steps
 
-    uniq, logical = unique_rows(reps[0]["sel"], reps[0]["cnt"], w, w.ctx)
+    uniq, logical = unique_rows(reps[0]["bits"], w, w.ctx)
     row_bytes = w.head_dim * w.elt_bytes
     gather_bytes = uniq * 2 * row_bytes
     kp_bytes = w.ctx * w.n_kv_heads * w.d_imp * w.elt_bytes

@@ -152,11 +152,12 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
  *   T = the first min(B, n) tokens of [0, n) ordered by (score descending,
  *       position ascending); -0.0 and +0.0 compare equal;
  *   S = union over t in T of [max(0, t-r), min(n-1, t+r)].
- * sel_idx[b][i][0 .. |S|) receives S ascending (stride
- * tb_selection_capacity()), sel_count[b][i] = |S|.  If topb_idx is not NULL
- * it receives T ascending with stride B (its count is min(B, n)).  If
+ * sel_count[b][i] = |S|.  If sel_idx is not NULL, sel_idx[b][i][0 .. |S|)
+ * receives S ascending (stride tb_selection_capacity()).  If topb_idx is not
+ * NULL it receives T ascending with stride B (its count is min(B, n)).  If
  * sel_bits is not NULL it receives S as a bitmap (all tb_bitmap_words()
- * words of the head are written; bits at positions >= n are zero).
+ * words of the head are written; bits at positions >= n are zero).  At
+ * least one of sel_idx and sel_bits must be given.
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
@@ -200,7 +201,7 @@ typedef struct tb_step_args {
     void *kp_cache;       /* [b][Hkv][ctx_cap][d] */
     const int32_t *ctx_len; /* [b]: context length AFTER the append */
     float softmax_scale;
-    int32_t *sel_idx;     /* state [b][Himp][tb_selection_capacity()] */
+    int32_t *sel_idx;     /* [b][Himp][tb_selection_capacity()] or NULL */
     int32_t *sel_count;   /* state [b][Himp] */
     uint32_t *sel_bits;   /* state [b][Himp][tb_bitmap_words()] */
     int32_t *keep_from;   /* state [b] */
@@ -218,8 +219,9 @@ typedef struct tb_step_args {
  *    [ctx_len[b] - n_new, ctx_len[b]) of the caches and their keys projected
  *    (as tb_project_keys).
  * 2. If refresh: scores over [0, ctx_len[b]) (as tb_score), T and S (as
- *    tb_select) are stored in sel_idx / sel_count / sel_bits, and
- *    keep_from[b] = ctx_len[b] - n_new.
+ *    tb_select) are stored in sel_count / sel_bits (and as the ascending
+ *    list in sel_idx when it is not NULL), and keep_from[b] = ctx_len[b] -
+ *    n_new.
  * 3. out = attention over S united with [keep_from[b], ctx_len[b]) (as
  *    tb_sparse_attn), so tokens appended since the last refresh are always
  *    attended.

@@ -171,7 +171,8 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
 {
     TB_TRY(check_shape(shape));
     TB_TRY(check_params(params));
-    if (scores == nullptr || ctx_len == nullptr || sel_idx == nullptr || sel_count == nullptr)
+    if (scores == nullptr || ctx_len == nullptr || sel_count == nullptr ||
+        (sel_idx == nullptr && sel_bits == nullptr))
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
@@ -212,8 +213,8 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     if (a == nullptr)
         return TB_EINVAL;
     if (a->q == nullptr || a->w == nullptr || a->k_cache == nullptr || a->v_cache == nullptr ||
-        a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_idx == nullptr ||
-        a->sel_count == nullptr || a->sel_bits == nullptr || a->keep_from == nullptr ||
+        a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_count == nullptr ||
+        a->sel_bits == nullptr || a->keep_from == nullptr ||
         a->out == nullptr)
         return TB_EINVAL;
     if (a->n_new < 0 || (a->n_new > 0 && (a->k_new == nullptr || a->v_new == nullptr)))

@@ -154,9 +154,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     __shared__ unsigned long long ubal[kMaxCounts];
     __shared__ uint32_t uoff[kMaxCounts];
     __shared__ uint32_t s_misc[4];
-    __shared__ float mrg_m[kAttnWaves][GQ];
-    __shared__ float mrg_l[kAttnWaves][GQ];
-    __shared__ float mrg_acc[kAttnWaves][GQ][D];
+    // slot merge: every row slot when it fits in LDS, else one slot per wave
+    constexpr bool kLdsMerge = 2048 * EPL * GQ <= 65536;
+    constexpr int NMS = kLdsMerge ? NSLOT : kAttnWaves;
+    __shared__ float mrg_m[NMS][GQ];
+    __shared__ float mrg_l[NMS][GQ];
+    __shared__ float mrg_f[NMS][GQ];
+    __shared__ float mrg_acc[NMS][GQ][D];
+    __shared__ float mrg_M[GQ], mrg_L[GQ];
     __shared__ float cmb_f[GQ][kMaxChunks];
     __shared__ float cmb_l[GQ][kMaxChunks];
     __shared__ float cmb_ml[GQ][2];
@@ -378,56 +383,73 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 consume(e[r], kk[r], vv[r]);
         }
 
-        // ---- 4. merge row slots (shuffles) and waves (LDS) into the chunk partial ----
+        // ---- 4. merge the row slots into the chunk partial ----
+        // Every slot's (max, sum, acc) goes to LDS; one wave per head finds
+        // the head's max and each slot's weight, then one thread per (head,
+        // dim) sums the weighted accumulators.  When that would not fit in
+        // LDS (8 bf16 query heads per KV head) slots are first merged within
+        // each wave by cross-lane shuffles.
+        constexpr int MSLOT = kLdsMerge ? NSLOT : kAttnWaves;
+        if constexpr (!kLdsMerge) {
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
+            for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-            for (int hl = 0; hl < GQ; ++hl) {
-                const float mo = __shfl_xor(m[hl], off);
-                const float lo_ = __shfl_xor(l[hl], off);
-                const float mn = fmaxf(m[hl], mo);
-                const float fa = m[hl] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hl] - mn);
-                const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
-                l[hl] = l[hl] * fa + lo_ * fb;
+                for (int hl = 0; hl < GQ; ++hl) {
+                    const float mo = __shfl_xor(m[hl], off);
+                    const float lo_ = __shfl_xor(l[hl], off);
+                    const float mn = fmaxf(m[hl], mo);
+                    const float fa = m[hl] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hl] - mn);
+                    const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+                    l[hl] = l[hl] * fa + lo_ * fb;
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) {
-                    const float ao = __shfl_xor(acc[hl][e], off);
-                    acc[hl][e] = acc[hl][e] * fa + ao * fb;
+                    for (int e = 0; e < EPL; ++e) {
+                        const float ao = __shfl_xor(acc[hl][e], off);
+                        acc[hl][e] = acc[hl][e] * fa + ao * fb;
+                    }
+                    m[hl] = mn;
                 }
-                m[hl] = mn;
             }
         }
-        if (slot == 0) {
+        if (kLdsMerge || slot == 0) {
+            const int ms = kLdsMerge ? wave * RPW + slot : wave;
 #pragma unroll
             for (int hl = 0; hl < GQ; ++hl) {
 #pragma unroll
                 for (int e = 0; e < EPL; ++e)
-                    mrg_acc[wave][hl][sub * EPL + e] = acc[hl][e];
+                    mrg_acc[ms][hl][sub * EPL + e] = acc[hl][e];
                 if (sub == 0) {
-                    mrg_m[wave][hl] = m[hl];
-                    mrg_l[wave][hl] = l[hl];
+                    mrg_m[ms][hl] = m[hl];
+                    mrg_l[ms][hl] = l[hl];
                 }
+            }
+        }
+        __syncthreads();
+        for (int hl = wave; hl < GQ; hl += kAttnWaves) {
+            const float mv = lane < MSLOT ? mrg_m[lane][hl] : -INFINITY;
+            float M = mv;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                M = fmaxf(M, __shfl_xor(M, off));
+            const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+            float Ls = lane < MSLOT ? mrg_l[lane][hl] * f : 0.f;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                Ls += __shfl_xor(Ls, off);
+            if (lane < MSLOT)
+                mrg_f[lane][hl] = f;
+            if (lane == 0) {
+                mrg_M[hl] = M;
+                mrg_L[hl] = Ls;
             }
         }
         __syncthreads();
         for (int pi = tid; pi < GQ * D; pi += kAttnThreads) {
             const int hl = pi / D, dim = pi % D;
-            float M = -INFINITY;
+            float O = 0.f;
 #pragma unroll
-            for (int s = 0; s < kAttnWaves; ++s)
-                M = fmaxf(M, mrg_m[s][hl]);
-            float Ls = 0.f, O = 0.f;
-            if (M != -INFINITY) {
-#pragma unroll
-                for (int s = 0; s < kAttnWaves; ++s) {
-                    const float ms = mrg_m[s][hl];
-                    if (ms != -INFINITY) {
-                        const float f = __builtin_amdgcn_exp2f(ms - M);
-                        Ls = fmaf(mrg_l[s][hl], f, Ls);
-                        O = fmaf(mrg_acc[s][hl][dim], f, O);
-                    }
-                }
-            }
+            for (int s2 = 0; s2 < MSLOT; ++s2)
+                O = fmaf(mrg_acc[s2][hl][dim], mrg_f[s2][hl], O);
+            const float M = mrg_M[hl], Ls = mrg_L[hl];
             const size_t pc = (head0 + hl) * nchunk + c;
             store_agent(&a.part_o[pc * D + dim], O);
             if (dim == 0)

@@ -5,25 +5,36 @@
 // tokens under a fixed budget B.  Inference Strategy > Optimizations: neighbor
 // fetching widens each kept token t to [t-r, t+r].
 //
-// One 1024-thread work-group per (sequence, importance head):
-//   1. Scores become order-preserving u32 keys (-0 folded onto +0).  Each
-//      thread owns whole 32-position words of the bitmap (word w = tid +
-//      j * 1024); up to two words (64 keys) per thread stay in registers, so
-//      the scores are read once, with 16-byte loads.
-//   2. Radix select from the top, 8 bits per pass, over the keys that match
-//      the prefix found so far.  Histograms live in LDS as 16 copies (lane
-//      mod 16), padded so that equal digits in different copies fall in
-//      different banks: at most four lanes of a wave hit one address.  A
-//      wave-wide suffix scan picks the digit holding the B-th largest key.
-//      When every key of that digit is needed the search stops early.
+// One 1024-thread work-group per (sequence, importance head).  Thread t owns
+// bitmap words w = t + 1024 j, i.e. the 32 positions 32w .. 32w+31.
+//   1. Scores become order-preserving u32 keys (-0 folded onto +0; positions
+//      >= n get key 0, below every real key).  Rows of up to 1024 words keep
+//      their keys in registers (read once, in 16-byte loads); longer rows
+//      re-read them (from L2) at each pass.
+//   2. The B-th largest key tau is bracketed from a sample of one position in
+//      eight (positions 8m): the sample goes into a 4096-bin histogram over
+//      its own key range, and two bins a safe margin either side of the
+//      sample quantile B/n bound a candidate key range.  One compare-only
+//      pass counts (by wave ballots) the keys above it and in it; when tau
+//      provably lies in the range and the candidates fit in LDS they are
+//      compacted there and the radix select below runs over them alone.
+//      Otherwise it runs over every key.
+//      Radix select: from the top, 8 bits per pass, over the keys that match
+//      the prefix found so far.  Over every key the histogram lives in LDS as
+//      16 copies (lane mod 16), padded so that equal digits in different
+//      copies fall in different banks; over the candidates one copy is
+//      enough.  A wave-wide suffix sum picks the digit holding the wanted
+//      key.  When every key of that digit is needed the search stops early.
 //      Result: the threshold tau and how many keys equal to it are kept (the
-//      lowest positions first).
+//      lowest positions first).  Either route gives the same tau.
 //   3. Every thread builds its own words of the kept set T from its keys; a
 //      block scan of per-word tie counts settles ties at tau by position.
 //   4. Dilation by r is word-wise shifts of the bitmap, clipped to [0, n).
-//   5. A block scan of per-word popcounts compacts the bitmap into the
-//      ascending index list; the bitmap itself can be written out too.
+//   5. A block scan of per-word popcounts gives |S| and, when the list is
+//      asked for, compacts the bitmap into the ascending index list; the
+//      bitmap itself can be written out too.
 #include "tb_internal.h"
+
 
 namespace tb {
 namespace {
@@ -32,6 +43,15 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kCopies = 16;
 constexpr int kCopyStride = 257; // words; the odd stride spreads copies over banks
+constexpr int kSampleBins = 4096;
+constexpr int kWaveCap = 512;       // candidates held per wave
+constexpr int kBinShift = 20;       // sample bins: the top 12 bits of a key
+constexpr int kMinSampleWords = 64; // shorter rows go straight to the full radix
+static_assert(kSampleBins == 64 * 64 && (1u << (32 - kBinShift)) == kSampleBins,
+              "64 sample bins per lane of one wave");
+static_assert(kSampleBins <= kCopies * kCopyStride, "sample histogram reuses the radix one");
+// misc words
+constexpr int kMiscScan = 8;   // kSelWaves + 1 words of block-scan scratch
 
 __device__ __forceinline__ uint32_t score_key(float s)
 {
@@ -41,8 +61,42 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of popcount(words[w]) over w < nw into out[w]; returns the
-// total to every thread.  wsum: kSelWaves + 1 words of LDS scratch.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts within rows of 16, then the
+// row totals are added across rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
+{
+    x += dpp<0x111>(x); // row_shr:1
+    x += dpp<0x112>(x); // row_shr:2
+    x += dpp<0x114>(x); // row_shr:4
+    x += dpp<0x118>(x); // row_shr:8
+    const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);
+    const uint32_t r1 = __builtin_amdgcn_readlane(x, 31);
+    const uint32_t r2 = __builtin_amdgcn_readlane(x, 47);
+    x += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+    return x;
+}
+
+// Wave-wide reduction (min, max or sum) through row permutations.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op)
+{
+    x = op(x, dpp<0xB1>(x));  // quad_perm [1,0,3,2]
+    x = op(x, dpp<0x4E>(x));  // quad_perm [2,3,0,1]
+    x = op(x, dpp<0x141>(x)); // row_half_mirror
+    x = op(x, dpp<0x140>(x)); // row_mirror
+    return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+              op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Exclusive scan of popcount(words[w]) over w < nw into out[w] (skipped when
+// out is NULL); returns the total to every thread.  wsum: kSelWaves words of
+// LDS scratch.
 __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int nw,
                                       uint32_t *wsum)
 {
@@ -52,37 +106,24 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
     uint32_t local = 0;
     for (int w = w0; w < w0 + per && w < nw; ++w)
         local += __popc(words[w]);
-    uint32_t inc = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_up(inc, off);
-        if (lane >= off)
-            inc += v;
-    }
+    const uint32_t inc = wave_incl_scan(local, lane);
     if (lane == 63)
         wsum[wave] = inc;
     __syncthreads();
-    if (wave == 0) {
-        const uint32_t v = lane < kSelWaves ? wsum[lane] : 0u;
-        uint32_t x = v;
+    uint32_t before = 0u, total = 0u;
 #pragma unroll
-        for (int off = 1; off < kSelWaves; off <<= 1) {
-            const uint32_t y = __shfl_up(x, off);
-            if (lane >= off)
-                x += y;
+    for (int v = 0; v < kSelWaves; ++v) {
+        const uint32_t x = wsum[v];
+        before += v < wave ? x : 0u;
+        total += x;
+    }
+    if (out != nullptr) {
+        uint32_t run = before + inc - local;
+        for (int w = w0; w < w0 + per && w < nw; ++w) {
+            out[w] = run;
+            run += __popc(words[w]);
         }
-        if (lane < kSelWaves)
-            wsum[lane] = x - v; // exclusive prefix of waves
-        if (lane == kSelWaves - 1)
-            wsum[kSelWaves] = x; // total
     }
-    __syncthreads();
-    uint32_t run = wsum[wave] + inc - local;
-    for (int w = w0; w < w0 + per && w < nw; ++w) {
-        out[w] = run;
-        run += __popc(words[w]);
-    }
-    const uint32_t total = wsum[kSelWaves];
     __syncthreads();
     return total;
 }
@@ -101,11 +142,92 @@ __device__ void compact_bits(const uint32_t *words, const uint32_t *offs, int nw
     }
 }
 
-// Loads the 32 keys of bitmap word w (positions >= n become key 0, which is
-// below every real key and never counted).  Whole words of 16-byte aligned
-// rows use four-float loads; a partial last word, or a row whose start is
-// not 16-byte aligned, is read one float at a time without touching
-// positions >= n.
+// Wave-wide digit choice: lane l holds the counts c of digits 4l .. 4l+3 of
+// the keys that match the prefix.  Finds the digit holding the krem-th
+// largest of them; afterwards, in every lane, prefix includes that digit
+// (at shift), krem is the rank left inside it and cnt is its count.
+__device__ __forceinline__ void pick_digit(uint4 c, int lane, int shift, uint32_t &prefix,
+                                           uint32_t &krem, uint32_t &cnt)
+{
+    const uint32_t sl = c.x + c.y + c.z + c.w;
+    const uint32_t inc = wave_incl_scan(sl, lane);
+    const uint32_t all = __builtin_amdgcn_readlane(inc, 63);
+    const uint32_t suf = all - inc + sl; // keys in digits >= 4 * lane
+    const unsigned long long m = __ballot(suf >= krem);
+    const int L = 63 - __clzll(m);
+    uint32_t above = suf - sl, dg, cd;
+    if (above + c.w >= krem) {
+        dg = 4u * lane + 3u;
+        cd = c.w;
+    } else if (above + c.w + c.z >= krem) {
+        above += c.w;
+        dg = 4u * lane + 2u;
+        cd = c.z;
+    } else if (above + c.w + c.z + c.y >= krem) {
+        above += c.w + c.z;
+        dg = 4u * lane + 1u;
+        cd = c.y;
+    } else {
+        above += c.w + c.z + c.y;
+        dg = 4u * lane;
+        cd = c.x;
+    }
+    prefix |= __builtin_amdgcn_readlane(dg, L) << shift;
+    krem -= __builtin_amdgcn_readlane(above, L);
+    cnt = __builtin_amdgcn_readlane(cd, L);
+}
+
+struct BinHit {
+    uint32_t bin;   // the bin holding the wanted rank
+    uint32_t above; // keys in the bins above it
+    uint32_t count; // keys in it
+};
+
+// One wave over a 4096-bin LDS histogram, read from the top: lane l sums
+// bins 64l .. 64l+63.  find(r) returns the bin holding the key of rank r
+// (0 = largest), r < total; every lane gets the same answer.
+struct BinScan {
+    uint32_t ls, above_l, total;
+    const uint32_t *h;
+    int lane;
+    __device__ BinScan(const uint32_t *hist, int lane_) : h(hist), lane(lane_)
+    {
+        uint32_t s = 0u;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const uint4 v = reinterpret_cast<const uint4 *>(hist)[lane * 16 + c];
+            s += v.x + v.y + v.z + v.w;
+        }
+        ls = s;
+        const uint32_t inc = wave_incl_scan(s, lane);
+        total = __builtin_amdgcn_readlane(inc, 63);
+        above_l = total - inc; // keys in bins above this lane's
+    }
+    __device__ BinHit find(uint32_t r) const
+    {
+        const unsigned long long m1 = __ballot(above_l <= r && r < above_l + ls);
+        const int L = __ffsll(m1) - 1;
+        const uint32_t aL = __builtin_amdgcn_readlane(above_l, L);
+        const uint32_t c = h[64 * L + lane];
+        const uint32_t inc = wave_incl_scan(c, lane);
+        const uint32_t up = aL + __builtin_amdgcn_readlane(inc, 63) - inc; // bins above 64L+lane
+        const unsigned long long m2 = __ballot(up <= r && r < up + c);
+        const int x = __ffsll(m2) - 1;
+        return BinHit{64u * L + (uint32_t)x, (uint32_t)__builtin_amdgcn_readlane(up, x),
+                      (uint32_t)__builtin_amdgcn_readlane(c, x)};
+    }
+    __device__ void clear(uint32_t *hist, int lane_) const
+    {
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            reinterpret_cast<uint4 *>(hist)[lane_ * 16 + c] = make_uint4(0u, 0u, 0u, 0u);
+    }
+};
+
+// Loads the 32 keys of bitmap word w (positions >= n become key 0).  Whole
+// words of 16-byte aligned rows use four-float loads; a partial last word, or
+// a row whose start is not 16-byte aligned, is read one float at a time
+// without touching positions >= n.
 __device__ __forceinline__ void load_word_keys(const float *row, int w, int n, bool vec,
                                                uint32_t (&k)[32])
 {
@@ -141,7 +263,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
     uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new)
 {
-    extern __shared__ uint32_t lds[];
+    extern __shared__ __align__(16) uint32_t lds[];
     uint32_t *hist = lds;                         // [kCopies][kCopyStride]
     uint32_t *tot = hist + kCopies * kCopyStride; // [256]
     uint32_t *misc = tot + 256;                   // 64 words
@@ -149,13 +271,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint32_t *Sb = Tb + nwc;                      // [nwc] widened set / tie bits
     uint32_t *Xb = Sb + nwc;                      // [nwc] dilation ping-pong
     uint32_t *scan = Xb + nwc;                    // [nwc] scan output
+    // candidates (key, position), kWaveCap per wave; shares Xb / scan,
+    // which are used only after the candidates are consumed
+    uint2 *cpair = reinterpret_cast<uint2 *>(Xb);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y, i = blockIdx.x;
     const size_t rowid = (size_t)b * Himp + i;
     const float *row = scores + rowid * cap;
     const int n = clamp_len(ctx_len[b], cap);
-    int32_t *out_sel = sel_idx + rowid * sel_stride;
     if (keep_from != nullptr && i == 0 && tid == 0)
         keep_from[b] = n - n_new > 0 ? n - n_new : 0;
     if (n == 0) {
@@ -167,139 +291,330 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         return;
     }
     const int nw = (n + 31) >> 5;
-    const int nwt = (nw + kSelThreads - 1) / kSelThreads; // words per thread (global mode)
+    const int nwt = (nw + kSelThreads - 1) / kSelThreads; // words per thread
     const bool vec = (cap & 3) == 0; // every row starts 16-byte aligned
+    if (tid < 64)
+        misc[tid] = 0u;
 
-    // Keys of this thread: keys[j][bit] is position (tid + j * kSelThreads) * 32 + bit.
-    constexpr int WR = WPT > 0 ? WPT : 1;
-    uint32_t keys[WR][32];
-    if constexpr (WPT > 0) {
-#pragma unroll
-        for (int j = 0; j < WR; ++j)
-            load_word_keys(row, tid + j * kSelThreads, n, vec, keys[j]);
-    }
-
-    const bool take_all = B >= n;
-    uint32_t tau = 0u, fmask = 0u, need = 0u, cnt_eq = 0u;
-    if (!take_all) {
-        for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
-            hist[e] = 0u;
-        __syncthreads();
-        uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
-        uint32_t *h = hist + (lane & (kCopies - 1)) * kCopyStride;
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            // key 0 marks a position >= n; real keys are never 0
-            auto count = [&](const uint32_t (&k)[32]) {
-#pragma unroll
-                for (int e = 0; e < 32; ++e)
-                    if (k[e] != 0u && (k[e] & pmask) == prefix)
-                        atomicAdd(&h[(k[e] >> shift) & 255u], 1u);
-            };
-            if constexpr (WPT > 0) {
-#pragma unroll
-                for (int j = 0; j < WR; ++j)
-                    count(keys[j]);
-            } else {
-                for (int j = 0; j < nwt; ++j) {
-                    uint32_t k[32];
-                    load_word_keys(row, tid + j * kSelThreads, n, vec, k);
-                    count(k);
-                }
+    uint32_t keys[32];
+    if constexpr (WPT > 0)
+        load_word_keys(row, tid, n, vec, keys);
+    // fn(w, k) over this thread's words, k[e] the key of position 32w + e
+    auto for_words = [&](auto &&fn) {
+        if constexpr (WPT > 0) {
+            fn(tid, keys);
+        } else {
+            for (int j = 0; j < nwt; ++j) {
+                uint32_t k[32];
+                load_word_keys(row, tid + j * kSelThreads, n, vec, k);
+                fn(tid + j * kSelThreads, k);
             }
-            __syncthreads();
+        }
+    };
+
+    // One radix pass.  count() adds the digit (bits shift..shift+7) of every
+    // key it visits that matches the prefix to the histogram (copy h16 when
+    // many, else copy 0).  Then misc[0] = the prefix extended by the digit
+    // that holds the krem-th largest of those keys, misc[1] = the rank left
+    // inside that digit and misc[2] = the digit's count.  The histogram is
+    // left zeroed.
+    uint32_t *h16 = hist + (lane & (kCopies - 1)) * kCopyStride;
+    auto radix_pass = [&](int shift, uint32_t prefix, uint32_t krem, bool many, auto &&count) {
+        count();
+        __syncthreads();
+        const uint32_t *src = hist;
+        if (many) {
             if (tid < 256) {
                 uint32_t cnt = 0u;
 #pragma unroll
                 for (int cp = 0; cp < kCopies; ++cp) {
                     cnt += hist[cp * kCopyStride + tid];
-                    hist[cp * kCopyStride + tid] = 0u; // ready for the next pass
+                    hist[cp * kCopyStride + tid] = 0u;
                 }
                 tot[tid] = cnt;
             }
             __syncthreads();
-            if (wave == 0) {
-                const uint32_t c0 = tot[4 * lane], c1 = tot[4 * lane + 1];
-                const uint32_t c2 = tot[4 * lane + 2], c3 = tot[4 * lane + 3];
-                const uint32_t sl = c0 + c1 + c2 + c3;
-                uint32_t suf = sl; // inclusive suffix sum over lanes
+            src = tot;
+        }
+        if (wave == 0) {
+            const uint4 c = reinterpret_cast<const uint4 *>(src)[lane];
+            if (!many)
+                reinterpret_cast<uint4 *>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
+            uint32_t pf = prefix, kr = krem, cd = 0u;
+            pick_digit(c, lane, shift, pf, kr, cd);
+            if (lane == 0) {
+                misc[0] = pf;
+                misc[1] = kr;
+                misc[2] = cd;
+            }
+        }
+        __syncthreads();
+    };
+
+    const bool take_all = B >= n;
+    uint32_t tau = 0u, fmask = 0xFFFFFFFFu, need = 0u, cnt_eq = 0u;
+    bool emitted = false; // Tb / Sb already hold the kept and tie bits
+    if (!take_all) {
+        // The sample histogram lives in the candidate area, which is not
+        // written before the histogram has been read.
+        uint32_t *shist = reinterpret_cast<uint32_t *>(cpair);
+        const bool sampled = nw >= kMinSampleWords;
+        for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+            hist[e] = 0u;
+        if (sampled)
+            for (int e = tid; e < kSampleBins; e += kSelThreads)
+                shist[e] = 0u;
+        __syncthreads();
+        bool found = false;
+        if (sampled) {
+            // ---- bracket tau from the keys at positions 8m ----
+            // (keys 0, 8, 16, 24 of every word), binned by their top 12 bits
+            auto sample_word = [&](int j, uint32_t (&s4)[4]) {
+                if constexpr (WPT > 0) {
+                    (void)j;
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t v = __shfl_down(suf, off);
-                    if (lane + off < 64)
-                        suf += v;
-                }
-                const unsigned long long m = __ballot(suf >= krem);
-                const int L = 63 - __clzll(m);
-                if (lane == L) {
-                    uint32_t above = suf - sl;
-                    uint32_t dg, cd;
-                    if (above + c3 >= krem) {
-                        dg = 4u * L + 3u;
-                        cd = c3;
-                    } else if (above + c3 + c2 >= krem) {
-                        above += c3;
-                        dg = 4u * L + 2u;
-                        cd = c2;
-                    } else if (above + c3 + c2 + c1 >= krem) {
-                        above += c3 + c2;
-                        dg = 4u * L + 1u;
-                        cd = c1;
-                    } else {
-                        above += c3 + c2 + c1;
-                        dg = 4u * L;
-                        cd = c0;
+                    for (int q = 0; q < 4; ++q)
+                        s4[q] = keys[8 * q];
+                } else {
+                    const int p0 = (tid + j * kSelThreads) * 32;
+                    float f[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int p = p0 + 8 * q;
+                        f[q] = row[p < n ? p : 0];
                     }
-                    misc[0] = prefix | (dg << shift);
-                    misc[1] = krem - above;
-                    misc[2] = cd;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        s4[q] = p0 + 8 * q < n ? score_key(f[q]) : 0u;
+                }
+            };
+            const int nsw = WPT > 0 ? 1 : nwt; // words sampled per thread
+            for (int j = 0; j < nsw; ++j) {
+                uint32_t s4[4];
+                sample_word(j, s4);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (s4[q] != 0u)
+                        atomicAdd(&shist[s4[q] >> kBinShift], 1u);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // sample ranks a margin either side of the expected rank of tau
+                const BinScan sc(shist, lane);
+                const float pb = (float)B / (float)n;
+                const float tr = pb * (float)sc.total;
+                const float mg = 4.5f * sqrtf((float)sc.total * pb * (1.f - pb)) + 3.f;
+                const int hi_rank = (int)floorf(tr - mg);
+                const int lo_rank = (int)ceilf(tr + mg);
+                uint32_t b_hi = kSampleBins - 1, b_lo = 0u;
+                if (hi_rank >= 0)
+                    b_hi = sc.find((uint32_t)hi_rank).bin;
+                if (lo_rank >= 1 && lo_rank <= (int)sc.total)
+                    b_lo = sc.find((uint32_t)lo_rank - 1u).bin;
+                if (lane == 0) {
+                    misc[4] = b_lo;
+                    misc[5] = b_hi;
                 }
             }
             __syncthreads();
-            prefix = misc[0];
-            krem = misc[1];
-            cnt_eq = misc[2];
-            pmask |= 255u << shift;
-            if (krem == cnt_eq)
-                break; // every key with this prefix is kept
+            // candidate range [plo, phim1]: bins b_lo .. b_hi; keys above are
+            // kept.  Candidates are also counted by their top 20 bits (bin and
+            // the next 8 bits) when their bins are few enough for that.
+            const uint32_t b_lo = misc[4], b_hi = misc[5];
+            const uint32_t plo = b_lo ? b_lo << kBinShift : 1u;
+            const uint32_t phim1 = (uint32_t)(((uint64_t)b_hi + 1u) << kBinShift) - 1u;
+            const uint32_t span = phim1 - plo;
+            const bool lvl = b_hi - b_lo < (uint32_t)(kSampleBins >> 8);
+            const uint32_t d0 = b_lo << 8; // first 20-bit prefix of the range
+            // ---- one pass: kept words of the keys above the range and
+            // candidate words; then the candidates (key, position), per wave ----
+            uint2 *cwave = cpair + wave * kWaveCap;
+            uint32_t run = 0u, na = 0u;
+            for_words([&](int w, const auto &k) {
+                uint32_t wt = 0u, wc = 0u;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    wt |= (uint32_t)(k[e] > phim1) << e;
+                    wc |= (uint32_t)(k[e] - plo <= span) << e;
+                }
+                if (w < nw) {
+                    Tb[w] = wt;
+                    Sb[w] = 0u;
+                }
+                na += __popc(wt);
+                // this lane's slots, after those of the lower lanes
+                const uint32_t c = __popc(wc);
+                const uint32_t inc = wave_incl_scan(c, lane);
+                uint32_t slot = run + inc - c;
+                run += __builtin_amdgcn_readlane(inc, 63);
+                // the few candidate keys are re-read (from cache), eight
+                // loads in flight at a time
+                while (wc) {
+                    int pos[8];
+                    bool ok[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        ok[t] = wc != 0u;
+                        pos[t] = w * 32 + (ok[t] ? __ffs(wc) - 1 : 0);
+                        wc &= wc - 1u;
+                    }
+                    float f[8];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t)
+                        f[t] = row[pos[t]];
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) {
+                        if (ok[t]) {
+                            const uint32_t kc = score_key(f[t]);
+                            if (slot < (uint32_t)kWaveCap)
+                                cwave[slot] = make_uint2(kc, (uint32_t)pos[t]);
+                            ++slot;
+                            if (lvl)
+                                atomicAdd(&hist[(kc >> 12) - d0], 1u);
+                        }
+                    }
+                }
+            });
+            na = wave_reduce(na, [](uint32_t x, uint32_t y) { return x + y; });
+            if (lane == 0) {
+                tot[wave] = run;
+                tot[kSelWaves + wave] = na;
+            }
+            __syncthreads();
+            uint32_t A = 0u, C = 0u;
+            bool over = false;
+#pragma unroll
+            for (int v = 0; v < kSelWaves; ++v) {
+                C += tot[v];
+                A += tot[kSelWaves + v];
+                over |= tot[v] > (uint32_t)kWaveCap;
+            }
+            found = lvl && !over && A < (uint32_t)B && (uint32_t)B <= A + C;
+            if (found) {
+                // ---- tau among the candidates: top 20 bits, then the rest ----
+                if (wave == 0) {
+                    const BinScan sc(hist, lane);
+                    const BinHit h = sc.find((uint32_t)B - A - 1u);
+                    sc.clear(hist, lane);
+                    if (lane == 0) {
+                        misc[0] = d0 + h.bin;          // 20-bit prefix of tau
+                        misc[1] = (uint32_t)B - A - h.above; // rank inside it
+                    }
+                }
+                __syncthreads();
+                const uint32_t p20 = misc[0];
+                for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                    if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
+                        const uint32_t kc = cpair[i].x;
+                        if ((kc >> 12) == p20)
+                            atomicAdd(&hist[kc & 4095u], 1u);
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    const uint32_t krem = misc[1];
+                    const BinScan sc(hist, lane);
+                    const BinHit h = sc.find(krem - 1u);
+                    if (lane == 0) {
+                        misc[2] = (p20 << 12) | h.bin; // tau
+                        misc[3] = krem - h.above;      // ties at tau kept
+                        misc[6] = h.count;             // keys equal to tau
+                    }
+                }
+                __syncthreads();
+                tau = misc[2];
+                need = misc[3];
+                cnt_eq = misc[6];
+                // candidates at or above tau join the kept words; those equal
+                // to tau are ties when ties are split
+                const bool split = need < cnt_eq;
+                for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                    if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
+                        const uint2 c = cpair[i];
+                        const uint32_t bit = 1u << (c.y & 31u);
+                        if (c.x > tau || (c.x == tau && !split))
+                            atomicOr(&Tb[c.y >> 5], bit);
+                        else if (c.x == tau)
+                            atomicOr(&Sb[c.y >> 5], bit);
+                    }
+                }
+                __syncthreads();
+                emitted = true;
+            } else {
+                for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+                    hist[e] = 0u;
+                __syncthreads();
+            }
         }
-        tau = prefix;
-        fmask = pmask;
-        need = krem; // keys equal to tau (under fmask) kept, lowest positions first
+        if (!found) {
+            // ---- radix select over every key ----
+            uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
+            for (int pass = 0; pass < 4; ++pass) {
+                const int shift = 24 - 8 * pass;
+                radix_pass(shift, prefix, krem, true, [&]() {
+                    for_words([&](int w, const auto &k) {
+                        (void)w;
+#pragma unroll
+                        for (int e = 0; e < 32; ++e)
+                            if (k[e] != 0u && (k[e] & pmask) == prefix)
+                                atomicAdd(&h16[(k[e] >> shift) & 255u], 1u);
+                    });
+                });
+                prefix = misc[0];
+                krem = misc[1];
+                cnt_eq = misc[2];
+                pmask |= 255u << shift;
+                if (krem == cnt_eq)
+                    break; // every key with this prefix is kept
+            }
+            tau = prefix;
+            fmask = pmask;
+            need = krem;
+        }
     }
+    // Kept: every valid key with (key & fmask) >= thr (every valid key when
+    // thr is 0, none when none_kept).  With split ties the keys with
+    // (key & fmask) == tau are ties, need of them kept, lowest positions first.
     const bool partial_ties = !take_all && need < cnt_eq;
+    uint32_t thr = 0u;
+    bool none_kept = false;
+    if (!take_all) {
+        if (!partial_ties)
+            thr = tau;
+        else if (tau == 0xFFFFFFFFu)
+            none_kept = true;
+        else
+            thr = tau + 1u;
+    }
 
     // ---- kept-set bitmap (and tie bitmap when ties are split) ----
-    auto emit = [&](int w, const uint32_t (&k)[32]) {
-        if (w >= nw)
-            return;
-        uint32_t gt = 0u, eq = 0u;
+    if (!emitted) {
+        for_words([&](int w, const auto &k) {
+            if (w >= nw)
+                return;
+            uint32_t wt = 0u, wq = 0u;
+            if (none_kept) {
+            } else if (thr == 0u) {
 #pragma unroll
-        for (int e = 0; e < 32; ++e) {
-            const uint32_t km = k[e] & fmask;
-            const bool valid = k[e] != 0u;
-            const bool in = valid && (take_all || km > tau || (!partial_ties && km == tau));
-            const bool tie = valid && partial_ties && km == tau;
-            gt |= (uint32_t)in << e;
-            eq |= (uint32_t)tie << e;
-        }
-        Tb[w] = gt;
-        Sb[w] = eq;
-    };
-    if constexpr (WPT > 0) {
+                for (int e = 0; e < 32; ++e)
+                    wt |= (uint32_t)(k[e] != 0u) << e;
+            } else {
 #pragma unroll
-        for (int j = 0; j < WR; ++j)
-            emit(tid + j * kSelThreads, keys[j]);
-    } else {
-        for (int j = 0; j < nwt; ++j) {
-            uint32_t k[32];
-            load_word_keys(row, tid + j * kSelThreads, n, vec, k);
-            emit(tid + j * kSelThreads, k);
-        }
+                for (int e = 0; e < 32; ++e)
+                    wt |= (uint32_t)((k[e] & fmask) >= thr) << e;
+            }
+            if (partial_ties) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e)
+                    wq |= (uint32_t)(k[e] != 0u && (k[e] & fmask) == tau) << e;
+            }
+            Tb[w] = wt;
+            Sb[w] = wq;
+        });
+        __syncthreads();
     }
-    __syncthreads();
     if (partial_ties) {
-        block_popc_exscan(Sb, scan, nw, misc + 8);
+        block_popc_exscan(Sb, scan, nw, misc + kMiscScan);
         for (int w = tid; w < nw; w += kSelThreads) {
             uint32_t e = Sb[w];
             const uint32_t pre = scan[w];
@@ -318,7 +633,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
     // ---- optional pre-widening output ----
     if (topb_idx != nullptr) {
-        block_popc_exscan(Tb, scan, nw, misc + 8);
+        block_popc_exscan(Tb, scan, nw, misc + kMiscScan);
         compact_bits(Tb, scan, nw, topb_idx + rowid * (size_t)B);
         __syncthreads();
     }
@@ -350,9 +665,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
     }
 
-    // ---- compaction into the ascending list (and the bitmap, if asked) ----
-    const uint32_t total = block_popc_exscan(fin, scan, nw, misc + 8);
-    compact_bits(fin, scan, nw, out_sel);
+    // ---- |S|, the ascending list (when asked) and the bitmap (when asked) ----
+    const uint32_t total =
+        block_popc_exscan(fin, sel_idx != nullptr ? scan : nullptr, nw, misc + kMiscScan);
+    if (sel_idx != nullptr)
+        compact_bits(fin, scan, nw, sel_idx + rowid * sel_stride);
     if (sel_bits != nullptr)
         for (int w = tid; w < bits_stride; w += kSelThreads)
             sel_bits[rowid * bits_stride + w] = w < nw ? fin[w] : 0u;
@@ -366,9 +683,13 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
                     int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
                     int32_t *keep_from, int n_new, hipStream_t st)
 {
-    const int nwc = (s.ctx_cap + 31) / 32 + 1;
-    const size_t lds =
-        ((size_t)kCopies * kCopyStride + 256 + 64 + 4 * (size_t)nwc) * sizeof(uint32_t);
+    // words per bitmap array, even so that the candidate pairs stay 8-byte aligned
+    const int nwc = ((s.ctx_cap + 31) / 32 + 2) & ~1;
+    const size_t u = 2 * (size_t)nwc > 2 * (size_t)kSelWaves * kWaveCap
+                         ? 2 * (size_t)nwc
+                         : 2 * (size_t)kSelWaves * kWaveCap;
+    const size_t lds = ((size_t)kCopies * kCopyStride + 256 + 64 + 2 * (size_t)nwc + u) *
+                       sizeof(uint32_t);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)select_kernel<WPT>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -392,9 +713,7 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
 {
 #define TB_SEL_ARGS                                                                          \
     s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from, n_new, st
-    const int words = (s.ctx_cap + 31) / 32;
-    if (words <= kSelThreads) return select_t<1>(TB_SEL_ARGS);
-    if (words <= 2 * kSelThreads) return select_t<2>(TB_SEL_ARGS);
+    if ((s.ctx_cap + 31) / 32 <= kSelThreads) return select_t<1>(TB_SEL_ARGS);
     return select_t<0>(TB_SEL_ARGS);
 #undef TB_SEL_ARGS
 }

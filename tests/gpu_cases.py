@@ -78,8 +78,10 @@ def device_case(w: Workload, layer: int = 0, pre: synth.Prefill | None = None) -
     return DeviceCase(w, pre, shape, params, cap_s, K, V, Kp, W, ws, sel, cnt, bits, keep)
 
 
-def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Tensor):
-    """tb_decode_step for step s (one appended token per sequence)."""
+def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Tensor,
+                   with_list: bool = True):
+    """tb_decode_step for step s (one appended token per sequence); without
+    the list the selection state is the bitmap alone."""
     w = dc.w
     ctx = torch.full((w.batch,), w.ctx0 + s + 1, dtype=torch.int32, device="cuda")
     q = inp.q.to("cuda")
@@ -88,8 +90,8 @@ def step_on_device(dc: DeviceCase, s: int, inp: synth.StepInputs, out: torch.Ten
     vn = inp.v_new.to("cuda")
     args = tbl.step_args(dc.shape, dc.params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=inp.refresh, w=dc.W,
                          k_cache=dc.K, v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
-                         softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
-                         sel_bits=dc.bits, keep_from=dc.keep, out=out)
+                         softmax_scale=w.softmax_scale, sel_idx=dc.sel if with_list else None,
+                         sel_count=dc.cnt, sel_bits=dc.bits, keep_from=dc.keep, out=out)
     tbl.decode_step(dc.shape, dc.params, args, dc.ws)
     torch.cuda.synchronize()
     return ctx

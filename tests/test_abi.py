@@ -121,6 +121,9 @@ def test_workspace_checks():
     misaligned = ctypes.c_void_p((1 << 20) + 8)
     assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, fake, fake, None, None,
                        misaligned, need, None) == tbl.TB_EINVAL
+    # the selection must go somewhere: a list, a bitmap or both
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, None, fake, None, None,
+                       fake, need, None) == tbl.TB_EINVAL
 
 
 def test_decode_step_argument_checks():

@@ -263,7 +263,12 @@ def _select_case(scores_rows, lens, B, r):
     topb = torch.full((bsz, H, B), -1, dtype=torch.int32, device="cuda")
     bits = torch.full((bsz, H, tbl.bitmap_words(shape)), -1, dtype=torch.int32, device="cuda")
     tbl.select(shape, params, sc, ctx, sel, cnt, ws, topb_idx=topb, sel_bits=bits)
+    # the bitmap alone (no list) carries the same selection
+    cnt2 = torch.full_like(cnt, -1)
+    bits2 = torch.full_like(bits, -1)
+    tbl.select(shape, params, sc, ctx, None, cnt2, ws, sel_bits=bits2)
     torch.cuda.synchronize()
+    assert torch.equal(cnt2, cnt) and torch.equal(bits2, bits)
     for b in range(bsz):
         n = lens[b]
         got = lists_of(sel, cnt, b)
@@ -285,6 +290,38 @@ def test_select_crafted_ties_and_signed_zeros(B, r):
     rows[:, 2] = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(3, cap))
     rows[:, 3] = 2.5                                                   # all equal
     _select_case(rows, [1, 777, 1500], B, r)
+
+
+def _long_rows(kind, bsz, H, cap, seed):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((bsz, H, cap)).astype(np.float32)
+    if kind == "gauss":
+        return g * 5.0
+    if kind == "levels":        # 4096 distinct values: ties at the threshold
+        return np.floor(g * 512.0).astype(np.float32)
+    if kind == "sample_low":    # every eighth position far below the rest
+        g[..., ::8] -= 100.0
+        return g
+    if kind == "sample_high":   # every eighth position far above the rest
+        g[..., ::8] += 100.0
+        return g
+    if kind == "narrow":        # all scores inside one binade
+        return (1.0 + np.abs(g) * 1e-3).astype(np.float32)
+    if kind == "equal":
+        return np.full((bsz, H, cap), -3.25, np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["gauss", "levels", "sample_low", "sample_high", "narrow",
+                                  "equal"])
+@pytest.mark.parametrize("cap,lens", [(32768, [32768, 20001, 2049]), (70000, [70000, 40000])])
+def test_select_long_rows(kind, cap, lens):
+    # long rows go through the sampled bracket of the threshold when it holds
+    # and through the full radix select when it does not; the kept set is
+    # the same either way
+    rows = _long_rows(kind, len(lens), 2, cap, seed=cap + len(kind))
+    for B, r in [(max(lens) // 10, 1), (1, 0), (lens[-1] - 1, 0), (4000, 2)]:
+        _select_case(rows, lens, B, r)
 
 
 def test_select_single_and_empty_contexts():
@@ -361,14 +398,17 @@ def test_attention_ignores_list_entries_beyond_context():
 
 
 def test_fused_step_is_deterministic():
+    # two runs give the same bits; the second keeps no list, only the bitmap
     w = LLAMA_32K
     outs = []
-    for _ in range(2):
+    for with_list in (True, False):
         dc = device_case(w)
         inp = synth.step_inputs(w, 0, dc.pre)
         out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
-        step_on_device(dc, 0, inp, out)
-        outs.append((out.clone(), dc.sel.clone(), dc.cnt.clone(), dc.bits.clone(),
-                     dc.Kp.clone()))
+        step_on_device(dc, 0, inp, out, with_list=with_list)
+        outs.append((out.clone(), dc.cnt.clone(), dc.bits.clone(), dc.Kp.clone(),
+                     dc.keep.clone()))
+        if with_list:
+            assert lists_of(dc.sel, dc.cnt, 0) == bitmap_positions(dc.bits, 0, w.ctx)
     for a, b in zip(*outs):
         assert torch.equal(a, b)
