@@ -41,17 +41,21 @@ constexpr int kMaxCounts = 1024;   // (mask group, position block, wave) ballot 
 // coherent with each other).  They are written and read with agent-scope
 // atomic accesses, which go through to the device coherence point, so no
 // full L2 write-back fence is needed to publish them.
-__device__ __forceinline__ void store_agent(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_agent(const float *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Two 64-bit accesses per four floats: every agent-scope access is its own
+// memory transaction, so wider ones matter.
 __device__ __forceinline__ float4 load4_agent(const float *p)
 {
-    return make_float4(load_agent(p), load_agent(p + 1), load_agent(p + 2), load_agent(p + 3));
+    const double x = __hip_atomic_load(reinterpret_cast<const double *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const double y = __hip_atomic_load(reinterpret_cast<const double *>(p) + 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float2 lo = __builtin_bit_cast(float2, x), hi = __builtin_bit_cast(float2, y);
+    return make_float4(lo.x, lo.y, hi.x, hi.y);
+}
+__device__ __forceinline__ void store2_agent(float *p, float x, float y)
+{
+    __hip_atomic_store(reinterpret_cast<double *>(p), __builtin_bit_cast(double, make_float2(x, y)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // First index e in [0, cnt] with L[e] >= v for an ascending list, found by
@@ -173,23 +177,41 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int nchunk = gridDim.x;
-    const int n = clamp_len(a.ctx_len[b], a.cap);
     const int c0 = c * kAttnChunk;
+    const size_t head0 = (size_t)b * a.Hq + (size_t)g * GQ; // first query head of the group
+    const int slot = lane / LPR, sub = lane % LPR;
+    static_assert(GQ * NWD <= kAttnThreads, "one bitmap word per thread");
+
+    // Everything that does not depend on the lengths is requested first: the
+    // q slice of this lane (kept in the storage type; bf16 pairs feed v_dot2)
+    // and, in bitmap mode, this thread's membership word.
+    uint4 qv[GQ];
+#pragma unroll
+    for (int hl = 0; hl < GQ; ++hl)
+        qv[hl] = *reinterpret_cast<const uint4 *>(q + (head0 + hl) * D + sub * EPL);
+    uint32_t word0 = 0u;
+    if constexpr (BITMAP) {
+        if (tid < GQ * NWD) {
+            const int hl = tid / NWD, w = tid % NWD;
+            const int i = (int)((long)(g * GQ + hl) * a.Himp / a.Hq);
+            const int p0 = c0 + 32 * w; // first position of this word
+            if (p0 < a.cap)
+                word0 = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride + (p0 >> 5)];
+        }
+    }
+    const int kf_raw = a.keep_from != nullptr ? a.keep_from[b] : a.cap;
+    const int n = clamp_len(a.ctx_len[b], a.cap);
     const int c1 = min(c0 + kAttnChunk, n);
     const bool active = c0 < n;
-    const size_t head0 = (size_t)b * a.Hq + (size_t)g * GQ; // first query head of the group
 
     if (active) {
         // ---- 1. per-head membership of this chunk ----
-        const int kf = a.keep_from != nullptr ? clamp_len(a.keep_from[b], n) : n;
+        const int kf = clamp_len(kf_raw, n);
         if constexpr (BITMAP) {
-            for (int e = tid; e < GQ * NWD; e += kAttnThreads) {
-                const int hl = e / NWD, w = e % NWD;
-                const int i = (int)((long)(g * GQ + hl) * a.Himp / a.Hq);
-                const int p0 = c0 + 32 * w; // first position of this word
-                uint32_t word = 0u;
-                if (p0 < c1)
-                    word = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride + (p0 >> 5)];
+            if (tid < GQ * NWD) {
+                const int hl = tid / NWD, w = tid % NWD;
+                const int p0 = c0 + 32 * w;
+                uint32_t word = p0 < c1 ? word0 : 0u;
                 // clip to [c0, c1) and add the always-kept range
                 const int lo = max(kf, p0), hi = min(c1, p0 + 32);
                 if (hi - p0 < 32)
@@ -270,13 +292,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                     c[j] = idx < NCNT ? (uint32_t)__popcll(ubal[idx]) : 0u;
                     sum += c[j];
                 }
-                uint32_t inc = sum;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t v = __shfl_up(inc, off);
-                    if (lane >= off)
-                        inc += v;
-                }
+                const uint32_t inc = wave_incl_scan(sum, lane);
                 uint32_t run = inc - sum;
 #pragma unroll
                 for (int j = 0; j < PERL; ++j) {
@@ -303,12 +319,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 
         // ---- 3. stream the rows ----
         const int nu = (int)s_misc[0];
-        const int slot = lane / LPR, sub = lane % LPR;
-        // q slice of this lane, kept in the storage type (bf16 pairs feed v_dot2)
-        uint4 qv[GQ];
-#pragma unroll
-        for (int hl = 0; hl < GQ; ++hl)
-            qv[hl] = *reinterpret_cast<const uint4 *>(q + (head0 + hl) * D + sub * EPL);
         float m[GQ], l[GQ], acc[GQ][EPL];
 #pragma unroll
         for (int hl = 0; hl < GQ; ++hl) {
@@ -426,15 +436,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         __syncthreads();
         for (int hl = wave; hl < GQ; hl += kAttnWaves) {
             const float mv = lane < MSLOT ? mrg_m[lane][hl] : -INFINITY;
-            float M = mv;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                M = fmaxf(M, __shfl_xor(M, off));
+            const float M = wave_max(mv);
             const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-            float Ls = lane < MSLOT ? mrg_l[lane][hl] * f : 0.f;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1)
-                Ls += __shfl_xor(Ls, off);
+            const float Ls = wave_sum(lane < MSLOT ? mrg_l[lane][hl] * f : 0.f);
             if (lane < MSLOT)
                 mrg_f[lane][hl] = f;
             if (lane == 0) {
@@ -443,6 +447,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             }
         }
         __syncthreads();
+        static_assert((GQ * D) % 64 == 0, "whole waves in the partial loop (lane pairs)");
         for (int pi = tid; pi < GQ * D; pi += kAttnThreads) {
             const int hl = pi / D, dim = pi % D;
             float O = 0.f;
@@ -451,7 +456,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 O = fmaf(mrg_acc[s2][hl][dim], mrg_f[s2][hl], O);
             const float M = mrg_M[hl], Ls = mrg_L[hl];
             const size_t pc = (head0 + hl) * nchunk + c;
-            store_agent(&a.part_o[pc * D + dim], O);
+            // even lanes store their own and the next lane's value (the
+            // next dimension of the same head) as one 64-bit access
+            const float On = __uint_as_float(dpp<0xB1>(__float_as_uint(O)));
+            if ((dim & 1) == 0)
+                store2_agent(&a.part_o[pc * D + dim], O, On);
             if (dim == 0)
                 __hip_atomic_store(reinterpret_cast<double *>(a.part_ml) + pc,
                                    __builtin_bit_cast(double, make_float2(M, Ls)),
@@ -508,9 +517,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         float M = -INFINITY;
         for (int cc = lane; cc < nact; cc += 64)
             M = fmaxf(M, cmb_f[hl][cc]);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            M = fmaxf(M, __shfl_xor(M, off));
+        M = wave_max(M);
         float Ls = 0.f;
         for (int cc = lane; cc < nact; cc += 64) {
             const float mc = cmb_f[hl][cc];
@@ -518,9 +525,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             cmb_f[hl][cc] = f;
             Ls = fmaf(cmb_l[hl][cc], f, Ls);
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1)
-            Ls += __shfl_xor(Ls, off);
+        Ls = wave_sum(Ls);
         if (lane == 0)
             cmb_ml[hl][0] = Ls;
     }

@@ -61,39 +61,6 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t x)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
-}
-
-// Inclusive prefix sum over the 64 lanes: shifts within rows of 16, then the
-// row totals are added across rows.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane)
-{
-    x += dpp<0x111>(x); // row_shr:1
-    x += dpp<0x112>(x); // row_shr:2
-    x += dpp<0x114>(x); // row_shr:4
-    x += dpp<0x118>(x); // row_shr:8
-    const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);
-    const uint32_t r1 = __builtin_amdgcn_readlane(x, 31);
-    const uint32_t r2 = __builtin_amdgcn_readlane(x, 47);
-    x += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
-    return x;
-}
-
-// Wave-wide reduction (min, max or sum) through row permutations.
-template <typename Op>
-__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op)
-{
-    x = op(x, dpp<0xB1>(x));  // quad_perm [1,0,3,2]
-    x = op(x, dpp<0x4E>(x));  // quad_perm [2,3,0,1]
-    x = op(x, dpp<0x141>(x)); // row_half_mirror
-    x = op(x, dpp<0x140>(x)); // row_mirror
-    return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
-              op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
-}
-
 // Exclusive scan of popcount(words[w]) over w < nw into out[w] (skipped when
 // out is NULL); returns the total to every thread.  wsum: kSelWaves words of
 // LDS scratch.
