@@ -12,16 +12,20 @@
 //      from its ascending selection list (the chunk's segment is located by a
 //      wave-parallel search, 64 samples per round); the always-kept range
 //      [keep_from, n) is added to every head.
-//   2. The union over the heads is compacted in LDS into (row, head mask)
-//      entries, so each selected K/V row is read from HBM once per group.
+//   2. Each query head is served by 8/GQ of the eight waves, each wave taking
+//      a part of the chunk and compacting that head's positions in it with
+//      ballots; the head's waves then split the concatenated list evenly.
+//      Rows that several query heads of the group select are requested by
+//      sibling waves of the same work-group at about the same time, so the
+//      repeats are served from cache and HBM sees each row about once.
 //   3. Rows stream through the lanes in 16-byte pieces (D*elt/16 lanes per
 //      row, several rows per wave, four rows in flight per row slot); each row
-//      slot keeps an online softmax (running max, sum, fp32 accumulator) per
-//      query head in base 2, rescaling only when the running max grows.  Lane
-//      dot products use v_dot2 on bf16 pairs and are reduced across the row's
-//      lanes with DPP row permutations.
-//   4. Row slots are merged by cross-lane shuffles, waves through LDS, into
-//      one partial (max, sum, acc[D]) per query head and chunk.
+//      slot keeps an online softmax (running max, sum, fp32 accumulator) for
+//      its wave's head in base 2, rescaling only when the running max grows.
+//      Lane dot products use v_dot2 on bf16 pairs and are reduced across the
+//      row's lanes with DPP row permutations.
+//   4. The row slots of a head are merged through LDS into one partial
+//      (max, sum, acc[D]) per query head and chunk.
 //   5. The last work-group of a (sequence, KV head) to arrive (device-scope
 //      counter) merges the chunk partials -- max and weights first, then the
 //      weighted sums with all of its threads -- writes the output rows, and
@@ -35,7 +39,6 @@ constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
 constexpr int kMaxChunks = kMaxCtxCap / kAttnChunk;
 constexpr int kRowsInFlight = 4; // rows per row slot loaded before use
-constexpr int kMaxCounts = 1024;   // (mask group, position block, wave) ballot counts
 
 // Chunk partials cross work-groups (and XCDs, whose L2 caches are not
 // coherent with each other).  They are written and read with agent-scope
@@ -150,21 +153,21 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave step
-    constexpr int NSLOT = kAttnWaves * RPW;  // row slots per work-group
     constexpr int NWD = kAttnChunk / 32;     // bitmap words per head
+    static_assert(GQ <= kAttnWaves && kAttnWaves % GQ == 0, "whole waves per query head");
+    constexpr int WPH = kAttnWaves / GQ;     // waves per query head
+    constexpr int PW = kAttnChunk / WPH;     // positions of one wave's part of the chunk
+    constexpr int NS = WPH * RPW;            // row slots per query head
+    static_assert(PW % 64 == 0 && NS <= 64, "parts of whole ballots; one lane per slot");
 
     __shared__ uint32_t bm[GQ][NWD];
-    __shared__ uint32_t ulist[kAttnChunk];
-    __shared__ unsigned long long ubal[kMaxCounts];
-    __shared__ uint32_t uoff[kMaxCounts];
+    __shared__ uint16_t hlist[kAttnWaves][PW]; // positions of each wave's part
+    __shared__ uint32_t wcnt[kAttnWaves];
     __shared__ uint32_t s_misc[4];
-    // slot merge: every row slot when it fits in LDS, else one slot per wave
-    constexpr bool kLdsMerge = 2048 * EPL * GQ <= 65536;
-    constexpr int NMS = kLdsMerge ? NSLOT : kAttnWaves;
-    __shared__ float mrg_m[NMS][GQ];
-    __shared__ float mrg_l[NMS][GQ];
-    __shared__ float mrg_f[NMS][GQ];
-    __shared__ float mrg_acc[NMS][GQ][D];
+    __shared__ float mrg_m[GQ][NS];
+    __shared__ float mrg_l[GQ][NS];
+    __shared__ float mrg_f[GQ][NS];
+    __shared__ float mrg_acc[GQ][NS][D];
     __shared__ float mrg_M[GQ], mrg_L[GQ];
     __shared__ float cmb_f[GQ][kMaxChunks];
     __shared__ float cmb_l[GQ][kMaxChunks];
@@ -182,13 +185,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int slot = lane / LPR, sub = lane % LPR;
     static_assert(GQ * NWD <= kAttnThreads, "one bitmap word per thread");
 
+    // Wave w serves query head hw = w / WPH on part w % WPH of the chunk.
+    const int hw = wave / WPH, wpart = wave % WPH;
     // Everything that does not depend on the lengths is requested first: the
-    // q slice of this lane (kept in the storage type; bf16 pairs feed v_dot2)
-    // and, in bitmap mode, this thread's membership word.
-    uint4 qv[GQ];
-#pragma unroll
-    for (int hl = 0; hl < GQ; ++hl)
-        qv[hl] = *reinterpret_cast<const uint4 *>(q + (head0 + hl) * D + sub * EPL);
+    // q slice of this lane for the wave's head (kept in the storage type;
+    // bf16 pairs feed v_dot2) and, in bitmap mode, this thread's membership
+    // word.
+    const uint4 qh = *reinterpret_cast<const uint4 *>(q + (head0 + hw) * D + sub * EPL);
     uint32_t word0 = 0u;
     if constexpr (BITMAP) {
         if (tid < GQ * NWD) {
@@ -248,214 +251,136 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         }
         __syncthreads();
 
-        // ---- 2. union over the heads, compacted with head masks ----
-        // Every thread owns positions tid, tid + kAttnThreads, ... of the chunk.
-        // For 2 or 4 query heads per KV head the entries are ordered by head
-        // mask, then by position, so the row slots of one wave mostly share a
-        // mask and heads that no slot needs are skipped as a whole; otherwise
-        // they are ordered by position.  The order is deterministic: offsets
-        // come from per-wave ballots and one wave-wide scan.
+        // ---- 2. this wave's positions, compacted by ballots ----
         {
-            constexpr int NIT = kAttnChunk / kAttnThreads;
-            constexpr int NGRP = (GQ == 2 || GQ == 4) ? (1 << GQ) - 1 : 1;
-            constexpr int NCNT = NGRP * NIT * kAttnWaves; // (group, it, wave), group-major
-            constexpr int PERL = (NCNT + 63) / 64;          // counts per lane of the scan
-            static_assert(NCNT <= kMaxCounts, "ballot table");
-            uint32_t tmask[NIT];
+            uint32_t run = 0u;
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int tl = it * kAttnThreads + tid;
-                uint32_t mk = 0u;
-#pragma unroll
-                for (int hl = 0; hl < GQ; ++hl)
-                    mk |= ((bm[hl][tl >> 5] >> (tl & 31)) & 1u) << hl;
-                tmask[it] = mk;
+            for (int k = 0; k < PW / 64; ++k) {
+                const int pos = wpart * PW + 64 * k + lane;
+                const bool in = (bm[hw][pos >> 5] >> (pos & 31)) & 1u;
+                const unsigned long long m = __ballot(in);
+                if (in)
+                    hlist[wave][run + __builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+                        (uint16_t)pos;
+                run += __popcll(m);
             }
-            auto group_of = [&](uint32_t mk) -> int { return NGRP == 1 ? 0 : (int)mk - 1; };
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-#pragma unroll
-                for (int gi = 0; gi < NGRP; ++gi) {
-                    const bool in = NGRP == 1 ? tmask[it] != 0u : tmask[it] == (uint32_t)(gi + 1);
-                    const unsigned long long bal = __ballot(in);
-                    if (lane == 0)
-                        ubal[(gi * NIT + it) * kAttnWaves + wave] = bal;
-                }
-            }
-            __syncthreads();
-            if (wave == 0) {
-                // exclusive scan of the NCNT ballot counts, PERL per lane
-                uint32_t c[PERL], sum = 0u;
-#pragma unroll
-                for (int j = 0; j < PERL; ++j) {
-                    const int idx = lane * PERL + j;
-                    c[j] = idx < NCNT ? (uint32_t)__popcll(ubal[idx]) : 0u;
-                    sum += c[j];
-                }
-                const uint32_t inc = wave_incl_scan(sum, lane);
-                uint32_t run = inc - sum;
-#pragma unroll
-                for (int j = 0; j < PERL; ++j) {
-                    const int idx = lane * PERL + j;
-                    if (idx < NCNT)
-                        uoff[idx] = run;
-                    run += c[j];
-                }
-                if (lane == 63)
-                    s_misc[0] = inc;
-            }
-            __syncthreads();
-            const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                if (tmask[it] != 0u) {
-                    const int idx = (group_of(tmask[it]) * NIT + it) * kAttnWaves + wave;
-                    const uint32_t pos = uoff[idx] + (uint32_t)__popcll(ubal[idx] & below);
-                    ulist[pos] = (uint32_t)(it * kAttnThreads + tid) | (tmask[it] << 16);
-                }
-            }
-            __syncthreads();
+            if (lane == 0)
+                wcnt[wave] = run;
         }
+        __syncthreads();
 
-        // ---- 3. stream the rows ----
-        const int nu = (int)s_misc[0];
-        float m[GQ], l[GQ], acc[GQ][EPL];
+        // ---- 3. stream the head's rows ----
+        // The head's positions are the concatenation of its WPH parts; each
+        // of its waves takes an equal share, and each row slot of a wave an
+        // interleaved share of that.
+        uint32_t pre[WPH], nh = 0u;
 #pragma unroll
-        for (int hl = 0; hl < GQ; ++hl) {
-            m[hl] = -INFINITY;
-            l[hl] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-                acc[hl][e] = 0.f;
+        for (int pp = 0; pp < WPH; ++pp) {
+            pre[pp] = nh;
+            nh += wcnt[hw * WPH + pp];
         }
-        const size_t kvbase = ((size_t)b * a.Hkv + g) * a.cap;
+        const uint32_t e0 = nh * wpart / WPH, e1 = nh * (wpart + 1) / WPH;
+        auto position = [&](uint32_t u) -> uint32_t { // u < nh
+            int src = hw * WPH;
+            uint32_t off = u;
+#pragma unroll
+            for (int pp = 1; pp < WPH; ++pp) {
+                const bool at = u >= pre[pp];
+                src = at ? hw * WPH + pp : src;
+                off = at ? u - pre[pp] : off;
+            }
+            return hlist[src][off];
+        };
+        float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+            acc[e] = 0.f;
+        const size_t kvbase = ((size_t)b * a.Hkv + g) * a.cap + c0;
         const T *kb = kc + kvbase * D + sub * EPL;
         const T *vb = vc + kvbase * D + sub * EPL;
 
-        // One row: for each query head that attends it, the logit (lane dot
-        // products reduced over the row's lanes), a running-max update that
-        // rescales only when the max grows, and the weighted V accumulation.
-        auto consume = [&](uint32_t ent, const uint4 &kp, const uint4 &vp) {
-            const uint32_t mask = ent >> 16;
-            float vf[EPL];
-            {
-                T vv[EPL];
-                __builtin_memcpy(vv, &vp, 16);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    vf[e] = to_f32(vv[e]);
-            }
-#pragma unroll
-            for (int hl = 0; hl < GQ; ++hl) {
-                if ((mask >> hl) & 1u) {
-                    const float z = group_sum<LPR>(lane_dot(qv[hl], kp)) * a.qscale;
-                    if (z > m[hl]) {
-                        const float corr = __builtin_amdgcn_exp2f(m[hl] - z);
-                        l[hl] *= corr;
-#pragma unroll
-                        for (int e = 0; e < EPL; ++e)
-                            acc[hl][e] *= corr;
-                        m[hl] = z;
-                    }
-                    const float p = __builtin_amdgcn_exp2f(z - m[hl]);
-                    l[hl] += p;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        acc[hl][e] = fmaf(p, vf[e], acc[hl][e]);
-                }
-            }
-        };
-        auto rowptr = [&](uint32_t ent) -> size_t {
-            return (size_t)(c0 + (int)(ent & 0xffffu)) * D;
-        };
-
         // All of a slot's rows (up to kRowsInFlight) are requested before any
         // is used.  The loads are unconditional -- a missing row reads the
-        // chunk's first row, which always exists, and is then skipped -- so
+        // chunk's first row, which always exists, and is given weight 0 -- so
         // they issue back to back.
-        for (int base = wave * RPW + slot; base < nu; base += kRowsInFlight * NSLOT) {
-            uint32_t e[kRowsInFlight];
+        for (uint32_t base = e0 + slot; base < e1; base += kRowsInFlight * RPW) {
+            uint32_t pos[kRowsInFlight];
+            bool ok[kRowsInFlight];
             uint4 kk[kRowsInFlight], vv[kRowsInFlight];
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
-                const int u = base + r * NSLOT;
-                e[r] = u < nu ? ulist[u] : 0u; // mask 0: nothing to do
+                const uint32_t u = base + r * RPW;
+                ok[r] = u < e1;
+                pos[r] = ok[r] ? position(u) : 0u;
             }
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
-                kk[r] = *reinterpret_cast<const uint4 *>(kb + rowptr(e[r]));
-                vv[r] = *reinterpret_cast<const uint4 *>(vb + rowptr(e[r]));
+                kk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pos[r] * D);
+                vv[r] = *reinterpret_cast<const uint4 *>(vb + (size_t)pos[r] * D);
             }
-            // consume() runs for every row (a missing row has an empty head
-            // mask and skips every head), so no load is sunk into a branch
 #pragma unroll
-            for (int r = 0; r < kRowsInFlight; ++r)
-                consume(e[r], kk[r], vv[r]);
+            for (int r = 0; r < kRowsInFlight; ++r) {
+                // logit in base 2, reduced over the row's lanes
+                const float z = group_sum<LPR>(lane_dot(qh, kk[r])) * a.qscale;
+                if (ok[r]) {
+                    if (z > m) {
+                        const float corr = __builtin_amdgcn_exp2f(m - z);
+                        l *= corr;
+#pragma unroll
+                        for (int e = 0; e < EPL; ++e)
+                            acc[e] *= corr;
+                        m = z;
+                    }
+                    const float pr = __builtin_amdgcn_exp2f(z - m);
+                    l += pr;
+                    T vt[EPL];
+                    __builtin_memcpy(vt, &vv[r], 16);
+#pragma unroll
+                    for (int e = 0; e < EPL; ++e)
+                        acc[e] = fmaf(pr, to_f32(vt[e]), acc[e]);
+                }
+            }
         }
 
-        // ---- 4. merge the row slots into the chunk partial ----
+        // ---- 4. merge each head's row slots into the chunk partial ----
         // Every slot's (max, sum, acc) goes to LDS; one wave per head finds
         // the head's max and each slot's weight, then one thread per (head,
-        // dim) sums the weighted accumulators.  When that would not fit in
-        // LDS (8 bf16 query heads per KV head) slots are first merged within
-        // each wave by cross-lane shuffles.
-        constexpr int MSLOT = kLdsMerge ? NSLOT : kAttnWaves;
-        if constexpr (!kLdsMerge) {
+        // dim) sums the weighted accumulators.
+        {
+            const int ms = wpart * RPW + slot;
 #pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-                for (int hl = 0; hl < GQ; ++hl) {
-                    const float mo = __shfl_xor(m[hl], off);
-                    const float lo_ = __shfl_xor(l[hl], off);
-                    const float mn = fmaxf(m[hl], mo);
-                    const float fa = m[hl] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hl] - mn);
-                    const float fb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
-                    l[hl] = l[hl] * fa + lo_ * fb;
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) {
-                        const float ao = __shfl_xor(acc[hl][e], off);
-                        acc[hl][e] = acc[hl][e] * fa + ao * fb;
-                    }
-                    m[hl] = mn;
-                }
-            }
-        }
-        if (kLdsMerge || slot == 0) {
-            const int ms = kLdsMerge ? wave * RPW + slot : wave;
-#pragma unroll
-            for (int hl = 0; hl < GQ; ++hl) {
-#pragma unroll
-                for (int e = 0; e < EPL; ++e)
-                    mrg_acc[ms][hl][sub * EPL + e] = acc[hl][e];
-                if (sub == 0) {
-                    mrg_m[ms][hl] = m[hl];
-                    mrg_l[ms][hl] = l[hl];
-                }
+            for (int e = 0; e < EPL; ++e)
+                mrg_acc[hw][ms][sub * EPL + e] = acc[e];
+            if (sub == 0) {
+                mrg_m[hw][ms] = m;
+                mrg_l[hw][ms] = l;
             }
         }
         __syncthreads();
-        for (int hl = wave; hl < GQ; hl += kAttnWaves) {
-            const float mv = lane < MSLOT ? mrg_m[lane][hl] : -INFINITY;
+        for (int h2 = wave; h2 < GQ; h2 += kAttnWaves) {
+            const float mv = lane < NS ? mrg_m[h2][lane] : -INFINITY;
             const float M = wave_max(mv);
             const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-            const float Ls = wave_sum(lane < MSLOT ? mrg_l[lane][hl] * f : 0.f);
-            if (lane < MSLOT)
-                mrg_f[lane][hl] = f;
+            const float Ls = wave_sum(lane < NS ? mrg_l[h2][lane] * f : 0.f);
+            if (lane < NS)
+                mrg_f[h2][lane] = f;
             if (lane == 0) {
-                mrg_M[hl] = M;
-                mrg_L[hl] = Ls;
+                mrg_M[h2] = M;
+                mrg_L[h2] = Ls;
             }
         }
         __syncthreads();
         static_assert((GQ * D) % 64 == 0, "whole waves in the partial loop (lane pairs)");
         for (int pi = tid; pi < GQ * D; pi += kAttnThreads) {
-            const int hl = pi / D, dim = pi % D;
+            const int h2 = pi / D, dim = pi % D;
             float O = 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < MSLOT; ++s2)
-                O = fmaf(mrg_acc[s2][hl][dim], mrg_f[s2][hl], O);
-            const float M = mrg_M[hl], Ls = mrg_L[hl];
-            const size_t pc = (head0 + hl) * nchunk + c;
+            for (int s2 = 0; s2 < NS; ++s2)
+                O = fmaf(mrg_acc[h2][s2][dim], mrg_f[h2][s2], O);
+            const float M = mrg_M[h2], Ls = mrg_L[h2];
+            const size_t pc = (head0 + h2) * nchunk + c;
             // even lanes store their own and the next lane's value (the
             // next dimension of the same head) as one 64-bit access
             const float On = __uint_as_float(dpp<0xB1>(__float_as_uint(O)));
