@@ -49,14 +49,17 @@
  *   multiply-add chains in ascending d_imp order starting from +0; attention
  *   accumulates in fp32.  Inputs must be finite.
  * - Alignment: tensors read or written in 16-byte pieces (K/V/Kp caches, q,
- *   W, k_new, v_new) must be 16-byte aligned, else TB_EINVAL.
+ *   W, k_new, v_new, the scores given to tb_select) must be 16-byte aligned,
+ *   else TB_EINVAL.
  * - Return value: TB_OK, or a negative TB_E* code.  Every argument check runs
  *   on the host before anything is enqueued, so an error return means nothing
  *   was launched -- except TB_EHIP, which reports a failed launch.
  * - Workspace: calls that take `ws` need at least tb_workspace_bytes() bytes
  *   of device memory, 256-byte aligned, ZERO-FILLED before its first use.
- *   Every call leaves it zero-filled where that matters, so one allocation
- *   can be reused; after a TB_EHIP error zero-fill it again.
+ *   Every call leaves it in a state the next call with the same shape
+ *   accepts, so one allocation can be reused; zero-fill it again after a
+ *   TB_EHIP error or before using it with another shape.  Calls that share
+ *   a workspace must not overlap.
  */
 #ifndef TOKENBUTLER_H
 #define TOKENBUTLER_H

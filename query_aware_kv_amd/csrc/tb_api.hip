@@ -174,6 +174,8 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
     if (scores == nullptr || ctx_len == nullptr || sel_count == nullptr ||
         (sel_idx == nullptr && sel_bits == nullptr))
         return TB_EINVAL;
+    if (!aligned16(scores))
+        return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,

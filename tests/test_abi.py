@@ -124,6 +124,9 @@ def test_workspace_checks():
     # the selection must go somewhere: a list, a bitmap or both
     assert L.tb_select(ctypes.byref(s), ctypes.byref(p), fake, fake, None, fake, None, None,
                        fake, need, None) == tbl.TB_EINVAL
+    # scores are read in 16-byte pieces
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(p), ctypes.c_void_p((1 << 20) + 4), fake,
+                       fake, fake, None, None, fake, need, None) == tbl.TB_EINVAL
 
 
 def test_decode_step_argument_checks():

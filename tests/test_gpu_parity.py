@@ -324,6 +324,38 @@ def test_select_long_rows(kind, cap, lens):
         _select_case(rows, lens, B, r)
 
 
+def test_select_many_rows_reused_workspace():
+    # more work-groups than the chip holds at once (4 x 32 rows of 32K
+    # positions, several work-groups per row), and one workspace reused by
+    # bitmap-only calls with different budgets: each call must match the
+    # list route, which the oracle checks
+    bsz, H, cap = 4, 32, 32768
+    lens = [32768, 30001, 16385, 4096]
+    rows = _long_rows("gauss", bsz, H, cap, seed=77)
+    _select_case(rows, lens, 3277, 1)
+    shape = tbl.make_shape(bsz, H, H, H, 64, 16, cap, torch.float32)
+    sc = torch.from_numpy(rows).cuda()
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = tbl.alloc_workspace(shape, tbl.make_params(4000, 2))
+    for B, r in [(3277, 1), (1000, 0), (4000, 2), (3277, 1)]:
+        params = tbl.make_params(B, r)
+        sel = torch.full((bsz, H, tbl.selection_capacity(shape, params)), -1, dtype=torch.int32,
+                         device="cuda")
+        cnt = torch.full((bsz, H), -1, dtype=torch.int32, device="cuda")
+        bits = torch.full((bsz, H, tbl.bitmap_words(shape)), -1, dtype=torch.int32, device="cuda")
+        tbl.select(shape, params, sc, ctx, sel, cnt, ws, sel_bits=bits)
+        cnt2 = torch.full_like(cnt, -1)
+        bits2 = torch.full_like(bits, -1)
+        tbl.select(shape, params, sc, ctx, None, cnt2, ws, sel_bits=bits2)
+        torch.cuda.synchronize()
+        assert torch.equal(cnt2, cnt) and torch.equal(bits2, bits), (B, r)
+        b = 1
+        got = lists_of(sel, cnt, b)
+        for i in (0, 31):
+            T_ref = orc.topb(rows[b, i, :lens[b]], B)
+            assert got[i] == orc.expand(T_ref, lens[b], r).tolist(), (B, r, i)
+
+
 def test_select_single_and_empty_contexts():
     rows = np.random.default_rng(5).standard_normal((2, 4, 64)).astype(np.float32)
     _select_case(rows, [0, 1], 3, 1)
