@@ -29,7 +29,8 @@ _lib = None
 
 def build(force: bool = False) -> str:
     """Compile ``tb_oracle.c`` into ``liboracle.so`` with gcc (CPU only)."""
-    if force or not os.path.exists(_LIB):
+    stale = not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
@@ -52,10 +53,15 @@ def _load():
         lib.orc_topb.restype = i32
         lib.orc_expand.argtypes = [P, i32, i32, i32, P]
         lib.orc_expand.restype = i32
+        lib.orc_buffers.argtypes = [i32, i32, i32, P, P]
+        lib.orc_buffers.restype = None
+        lib.orc_select.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
+        lib.orc_select.restype = i32
         lib.orc_attend.argtypes = [P, P, P, ctypes.c_int, P, i32, dbl, P, P]
         lib.orc_decode_step.argtypes = (
             [ctypes.c_int] * 7 + [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, dbl,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, dbl,
                                   P, P, P, ctypes.c_int, P])
         lib.orc_decode_step.restype = ctypes.c_int
         _lib = lib
@@ -144,9 +150,31 @@ def attend(q, K, V, S, scale: float, return_weights: bool = False):
     return out
 
 
-def cap_s(cap: int, B: int, r: int) -> int:
-    """Capacity of one head's stored selection: min(cap, (2r+1) B)."""
-    return min(cap, (2 * r + 1) * B)
+def buffers(n: int, n_sink: int, n_local: int):
+    """(lo, hi): the sink is [0, lo), the local window [hi, n), the middle
+    region between them."""
+    lo = ctypes.c_int32()
+    hi = ctypes.c_int32()
+    _load().orc_buffers(int(n), int(n_sink), int(n_local), ctypes.byref(lo), ctypes.byref(hi))
+    return lo.value, hi.value
+
+
+def select(s32, B: int, r: int, n_sink: int = 0, n_local: int = 0):
+    """(T, S) of one head over a context of s32.size tokens: T the top-B of
+    the middle region, S = widen(T, r) united with the sink and local window."""
+    s = np.ascontiguousarray(s32, dtype=np.float32)
+    n = s.size
+    T = np.empty(max(n, 1), dtype=np.int32)
+    S = np.empty(max(n, 1), dtype=np.int32)
+    nT = ctypes.c_int32()
+    c = _load().orc_select(_p(s), n, int(B), int(r), int(n_sink), int(n_local), _p(T),
+                           ctypes.byref(nT), _p(S))
+    return T[:nT.value].copy(), S[:c].copy()
+
+
+def cap_s(cap: int, B: int, r: int, n_sink: int = 0, n_local: int = 0) -> int:
+    """Capacity of one head's stored selection: min(cap, (2r+1) B + n_sink + n_local)."""
+    return min(cap, (2 * r + 1) * B + n_sink + n_local)
 
 
 class SequenceState:
@@ -155,7 +183,7 @@ class SequenceState:
     K, V [Hkv, cap, D], Kp [Hkv, cap, d] as float64; sel [Himp, cap_S] int32,
     cnt [Himp] int32, keep_from [1] int32."""
 
-    def __init__(self, K, V, Kp, Himp: int, B: int, r: int):
+    def __init__(self, K, V, Kp, Himp: int, B: int, r: int, n_sink: int = 0, n_local: int = 0):
         self.K = _f64(K).copy()
         self.V = _f64(V).copy()
         self.Kp = _f64(Kp).copy()
@@ -163,7 +191,9 @@ class SequenceState:
         self.cap = cap
         self.B = int(B)
         self.r = int(r)
-        self.cap_S = cap_s(cap, B, r)
+        self.n_sink = int(n_sink)
+        self.n_local = int(n_local)
+        self.cap_S = cap_s(cap, B, r, n_sink, n_local)
         self.sel = np.zeros((Himp, self.cap_S), dtype=np.int32)
         self.cnt = np.zeros(Himp, dtype=np.int32)
         self.keep_from = np.zeros(1, dtype=np.int32)
@@ -193,7 +223,7 @@ def decode_step(st: SequenceState, W, q, q_imp, ctx: int, dtype: int, refresh: b
     rc = _load().orc_decode_step(
         Hq, Hkv, Himp, D, d, cap, dtype, _p(st.K), _p(st.V), _p(st.Kp), _p(W),
         _p(kn), _p(vn), n_new, int(ctx), _p(q), _p(qi), int(bool(refresh)), st.B, st.r,
-        float(scale), _p(st.sel), _p(st.cnt), _p(st.keep_from), st.cap_S, _p(out))
+        st.n_sink, st.n_local, float(scale), _p(st.sel), _p(st.cnt), _p(st.keep_from), st.cap_S, _p(out))
     if rc != 0:
         raise RuntimeError("oracle decode_step: selection exceeds its capacity")
     return out

@@ -31,6 +31,11 @@
  *     tie.  If B >= n every token is kept.
  *   - Neighbor fetching widens every kept token t to [t-r, t+r] clipped to
  *     [0, n); the union is deduplicated and the budget is not re-applied.
+ *   - Sink and local window ([INF], the three buffers): the first n_sink
+ *     positions and the last n_local positions of [0, n) are always kept.
+ *     The three buffers partition the cache, so the top-B choice is made
+ *     among the remaining (middle) positions only; the widened choice is
+ *     then united with both ranges.
  *   - Attention is exact softmax attention with logits scaled by the given
  *     softmax scale, computed over the attended set only.
  *   - An empty attended set yields a zero output row.
@@ -206,6 +211,64 @@ int32_t orc_expand(const int32_t *T, int32_t nT, int32_t n, int32_t r, int32_t *
 }
 
 /* ------------------------------------------------------------------ */
+/* The three buffers ([INF]: sink, local window, important)            */
+/* ------------------------------------------------------------------ */
+
+/* Bounds of the middle region [*lo, *hi) of a context of n tokens: the sink
+ * is [0, *lo), the local window [*hi, n). */
+void orc_buffers(int32_t n, int32_t n_sink, int32_t n_local, int32_t *lo, int32_t *hi)
+{
+    int32_t a = n_sink < n ? n_sink : n;
+    int32_t b = n - n_local;
+    if (b < a)
+        b = a;
+    *lo = a;
+    *hi = b;
+}
+
+/* One head's kept set S over a context of n tokens: the important buffer is
+ * the top-B tokens of the middle region (T, written to T when not NULL),
+ * widened by r; S is its union with the sink and the local window, in
+ * ascending order.  Returns |S|; *nT receives |T|. */
+int32_t orc_select(const float *s, int32_t n, int32_t B, int32_t r, int32_t n_sink,
+                   int32_t n_local, int32_t *T, int32_t *nT, int32_t *S)
+{
+    if (n <= 0) {
+        *nT = 0;
+        return 0;
+    }
+    int32_t lo, hi;
+    orc_buffers(n, n_sink, n_local, &lo, &hi);
+    int32_t *Tm = (int32_t *)malloc((size_t)n * sizeof(int32_t));
+    int32_t *E = (int32_t *)malloc((size_t)n * sizeof(int32_t));
+    /* 1. important buffer: top-B of the middle region, back in context positions */
+    int32_t m = orc_topb(s + lo, hi - lo, B, Tm);
+    for (int32_t k = 0; k < m; ++k)
+        Tm[k] += lo;
+    /* 2. neighbor fetching */
+    int32_t ne = orc_expand(Tm, m, n, r, E);
+    /* 3. union with the sink [0, lo) and the local window [hi, n) */
+    char *in = (char *)calloc((size_t)n, 1);
+    for (int32_t k = 0; k < ne; ++k)
+        in[E[k]] = 1;
+    for (int32_t t = 0; t < lo; ++t)
+        in[t] = 1;
+    for (int32_t t = hi; t < n; ++t)
+        in[t] = 1;
+    int32_t c = 0;
+    for (int32_t t = 0; t < n; ++t)
+        if (in[t])
+            S[c++] = t;
+    if (T)
+        memcpy(T, Tm, (size_t)m * sizeof(int32_t));
+    *nT = m;
+    free(in);
+    free(E);
+    free(Tm);
+    return c;
+}
+
+/* ------------------------------------------------------------------ */
 /* Attention over the selected rows only ([ABS]; [SIG])                */
 /* ------------------------------------------------------------------ */
 
@@ -264,7 +327,8 @@ void orc_attend(const double *q, const double *K, const double *V, int D,
  *
  * ctx is the context length after the append; the new rows occupy
  * [ctx - n_new, ctx).  On a refresh step every importance head is scored over
- * [0, ctx), its top-B set is taken and widened by radius r, the result is
+ * [0, ctx), its kept set is taken (orc_select: top-B of the middle region
+ * widened by radius r, plus the sink and the local window), the result is
  * stored in sel/cnt and keep_from is set to ctx - n_new.  Every step then
  * attends, for query head h, over sel[imp(h)] united with [keep_from, ctx).
  * Returns 0, or -1 when a stored set would overflow cap_S.
@@ -273,8 +337,8 @@ int orc_decode_step(int Hq, int Hkv, int Himp, int D, int d, int cap, int dtype,
                     double *K, double *V, double *Kp, const double *W,
                     const double *k_new, const double *v_new, int n_new, int ctx,
                     const double *q, const double *q_imp, int refresh, int B, int r,
-                    double scale, int32_t *sel, int32_t *cnt, int32_t *keep_from,
-                    int cap_S, double *out)
+                    int n_sink, int n_local, double scale, int32_t *sel, int32_t *cnt,
+                    int32_t *keep_from, int cap_S, double *out)
 {
     /* 1. append the new rows and project their keys */
     for (int j = 0; j < n_new; ++j) {
@@ -297,8 +361,8 @@ int orc_decode_step(int Hq, int Hkv, int Himp, int D, int d, int cap, int dtype,
             int g = imp_group(i, Himp, Hkv);
             orc_score(q_imp + (int64_t)i * d, Kp + (int64_t)g * cap * d, 1, 1, cap, d, ctx,
                       NULL, s);
-            int32_t nT = orc_topb(s, ctx, B, T);
-            int32_t nS = orc_expand(T, nT, ctx, r, S);
+            int32_t nT = 0;
+            int32_t nS = orc_select(s, ctx, B, r, n_sink, n_local, T, &nT, S);
             if (nS > cap_S) {
                 free(s);
                 free(T);

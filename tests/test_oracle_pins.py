@@ -278,6 +278,66 @@ def test_expand_golden_hand_cases():
         assert orc.expand(c["T"], c["n"], c["r"]).tolist() == c["expected"], c
 
 
+# --------------------------------------------------------------------------
+# sink, local window and important buffer
+# --------------------------------------------------------------------------
+
+def test_select_buffers_golden_hand_cases():
+    for c in _golden("select_buffers_cases.json")["cases"]:
+        s = np.array(c["scores"], dtype=np.float32)
+        T, S = orc.select(s, c["budget"], c["radius"], c["n_sink"], c["n_local"])
+        assert T.tolist() == c["T"], c
+        assert S.tolist() == c["expected"], c
+
+
+def _select_brute(s, B, r, n_sink, n_local):
+    # independent formulation: membership tests position by position
+    n = s.size
+    lo = min(n_sink, n)
+    hi = max(lo, n - n_local)
+    T = [i for i in range(lo, hi)
+         if sum(1 for j in range(lo, hi) if s[j] > s[i] or (s[j] == s[i] and j < i)) < B]
+    S = [t for t in range(n)
+         if t < lo or t >= hi or any(abs(t - i) <= r for i in T)]
+    return T, S
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_select_buffers_brute_force(seed):
+    rng = np.random.default_rng(900 + seed)
+    n = int(rng.integers(1, 40))
+    if seed % 3 == 0:
+        s = rng.integers(-2, 3, size=n).astype(np.float32)     # heavy ties
+    elif seed % 3 == 1:
+        s = rng.choice(np.array([-0.0, 0.0, 1.0], np.float32), size=n)
+    else:
+        s = rng.standard_normal(n).astype(np.float32)
+    for _ in range(4):
+        B = int(rng.integers(1, n + 3))
+        r = int(rng.integers(0, 4))
+        ns, nl = int(rng.integers(0, n + 2)), int(rng.integers(0, n + 2))
+        T, S = orc.select(s, B, r, ns, nl)
+        Tb, Sb = _select_brute(s, B, r, ns, nl)
+        assert T.tolist() == Tb and S.tolist() == Sb, (n, B, r, ns, nl)
+        assert len(S) <= orc.cap_s(n, B, r, ns, nl)
+
+
+def test_select_without_buffers_is_topb_then_expand():
+    s = np.random.default_rng(3).standard_normal(50).astype(np.float32)
+    for B, r in [(1, 0), (7, 2), (60, 1)]:
+        T, S = orc.select(s, B, r)
+        assert T.tolist() == orc.topb(s, B).tolist()
+        assert S.tolist() == orc.expand(orc.topb(s, B), 50, r).tolist()
+
+
+def test_buffers_bounds():
+    assert orc.buffers(10, 2, 3) == (2, 7)
+    assert orc.buffers(10, 0, 0) == (0, 10)
+    assert orc.buffers(5, 7, 0) == (5, 5)
+    assert orc.buffers(5, 3, 4) == (3, 3)
+    assert orc.buffers(0, 3, 4) == (0, 0)
+
+
 def _expand_by_convolution(T, n, r):
     # independent formulation: dilate the indicator with a box filter
     ind = np.zeros(n)
@@ -386,8 +446,9 @@ def _one_hot_sequence(scores, D):
     return K, V, W
 
 
-def test_interval_golden_hand_case():
-    g = _golden("interval_case.json")
+@pytest.mark.parametrize("name", ["interval_case.json", "interval_buffers_case.json"])
+def test_interval_golden_hand_case(name):
+    g = _golden(name)
     scores = g["scores_by_position"]
     n_total = len(scores)
     D = 16
@@ -399,7 +460,8 @@ def test_interval_golden_hand_case():
     Kc[0, :ctx0] = K[:ctx0]
     Vc[0, :ctx0] = V[:ctx0]
     Kp = orc.project(Kc, W, orc.F32)
-    st = orc.SequenceState(Kc, Vc, Kp, Himp=1, B=g["budget"], r=g["radius"])
+    st = orc.SequenceState(Kc, Vc, Kp, Himp=1, B=g["budget"], r=g["radius"],
+                           n_sink=g.get("n_sink", 0), n_local=g.get("n_local", 0))
     for s, attended in enumerate(g["attended_by_step"]):
         ctx = ctx0 + s + 1
         refresh = s % g["interval"] == 0
