@@ -12,6 +12,8 @@ serve one step's reads from the previous steps.
 Prints one JSON line.  Extra legs:
   roofline      the attention kernel (the step's largest HBM consumer), timed
                 with HIP events on its stream over K launches, against 8 TB/s;
+  dense_attention  the dense decode-attention kernel over the whole context at
+                the same shape (the baseline of the pages' speedup claims);
   cpu_baseline  the fp64 C oracle's decode step on the host (1 thread), on a
                 bounded number of steps.
 """
@@ -19,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+from dataclasses import replace
 import os
 import sys
 import time
@@ -110,6 +113,10 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-sink", type=int, default=0,
+                    help="tokens always kept at the start of the context (sink buffer)")
+    ap.add_argument("--n-local", type=int, default=0,
+                    help="most recent tokens always kept (local window)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
@@ -121,7 +128,7 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
 
-    w = LLAMA_32K
+    w = replace(LLAMA_32K, n_sink=a.n_sink, n_local=a.n_local)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(f"bench: generating {w.name}")
@@ -129,7 +136,7 @@ def main() -> int:
     inp = synth.step_inputs(w, 0, pre)
     shape = tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
                            w.d_imp, w.ctx_cap, synth.torch_dtype(w))
-    params = tbl.make_params(w.budget, w.radius)
+    params = tbl.make_params(w.budget, w.radius, w.n_sink, w.n_local)
 
     K0, V0, W = pre.K.to(dev), pre.V.to(dev), pre.W.to(dev)
     Kp0 = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=K0.dtype, device=dev)
@@ -187,6 +194,19 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_attn = e0.elapsed_time(e1) / a.steps
 
+    # comparator: dense attention over the whole context at the same shape
+    for s in range(a.warmup):
+        r = reps[s % R]
+        tbl.dense_attn(shape, q, r["K"], r["V"], ctx, w.softmax_scale, out, ws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(a.steps):
+        r = reps[s % R]
+        tbl.dense_attn(shape, q, r["K"], r["V"], ctx, w.softmax_scale, out, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_dense = e0.elapsed_time(e1) / a.steps
+
     uniq, logical = unique_rows(reps[0]["bits"], w, w.ctx)
     row_bytes = w.head_dim * w.elt_bytes
     gather_bytes = uniq * 2 * row_bytes
@@ -194,8 +214,12 @@ def main() -> int:
     step_bytes = kp_bytes + gather_bytes
     attn_gbs = gather_bytes / (ms_attn * 1e-3) / 1e9
     step_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    dense_bytes = w.ctx * w.n_kv_heads * 2 * row_bytes
+    dense_gbs = dense_bytes / (ms_dense * 1e-3) / 1e9
     log(f"bench: attention {ms_attn * 1e3:.2f} us, {attn_gbs:.0f} GB/s; step {step_gbs:.0f} GB/s "
         f"({uniq} unique rows, {logical} logical)")
+    log(f"bench: dense attention {ms_dense * 1e3:.2f} us, {dense_gbs:.0f} GB/s; "
+        f"sparse step / dense attention = {ms_dense / ms_step:.2f}x")
 
     if a.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -226,6 +250,7 @@ def main() -> int:
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
                    "imp_heads": w.n_imp_heads, "head_dim": w.head_dim, "d_imp": w.d_imp,
                    "budget": w.budget, "radius": w.radius, "interval": w.interval,
+                   "n_sink": w.n_sink, "n_local": w.n_local,
                    "storage": w.dtype, "replicas": R},
         "roofline": {"bound": "hbm", "kernel": "attn_kernel (tb_sparse_attn)",
                      "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -234,6 +259,10 @@ def main() -> int:
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
                      "frac": step_gbs / PEAK_HBM_GBS, "unique_rows": uniq,
                      "logical_rows": logical},
+        "dense_attention": {"kernel": "dense_kernel (tb_dense_attn)", "us_per_launch": ms_dense * 1e3,
+                            "algorithmic_bytes": dense_bytes, "achieved": dense_gbs,
+                            "frac": dense_gbs / PEAK_HBM_GBS,
+                            "speedup_of_sparse_step": ms_dense / ms_step},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -94,8 +94,8 @@ typedef struct tb_shape {
 typedef struct tb_select_params {
     int32_t budget;  /* B >= 1: tokens kept per importance head before widening */
     int32_t radius;  /* r in [0, 1024]: neighbor-fetch radius */
-    int32_t n_sink;  /* reserved, must be 0 */
-    int32_t n_local; /* reserved, must be 0 */
+    int32_t n_sink;  /* >= 0: the first n_sink tokens are always kept ([INF] sink) */
+    int32_t n_local; /* >= 0: the last n_local tokens are always kept ([INF] local window) */
 } tb_select_params;
 
 /* Library version (major*10000 + minor*100 + patch).  Host only. */
@@ -149,15 +149,21 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
 /*
  * tb_select -- per-head top-B under a fixed budget, then neighbor fetching.
  * [ABS], [ARCH]: per-token selection of the highest-scoring tokens under a
- * fixed budget; [INF]: each kept token is widened to its spatial neighbors.
+ * fixed budget; [INF]: each kept token is widened to its spatial neighbors,
+ * and the cache is split into a sink, a local window and the important
+ * buffer that the scores fill.
  *
- * For each (b, i) with n = ctx_len[b]:
- *   T = the first min(B, n) tokens of [0, n) ordered by (score descending,
- *       position ascending); -0.0 and +0.0 compare equal;
- *   S = union over t in T of [max(0, t-r), min(n-1, t+r)].
+ * For each (b, i) with n = ctx_len[b], lo = min(n_sink, n) and
+ * hi = max(lo, n - n_local) (the middle region is [lo, hi)):
+ *   T = the first min(B, hi - lo) tokens of [lo, hi) ordered by (score
+ *       descending, position ascending); -0.0 and +0.0 compare equal;
+ *   S = union over t in T of [max(0, t-r), min(n-1, t+r)], united with the
+ *       sink [0, lo) and the local window [hi, n).
+ * With n_sink = n_local = 0 this is plain top-B over [0, n) then widening.
  * sel_count[b][i] = |S|.  If sel_idx is not NULL, sel_idx[b][i][0 .. |S|)
- * receives S ascending (stride tb_selection_capacity()).  If topb_idx is not
- * NULL it receives T ascending with stride B (its count is min(B, n)).  If
+ * receives S ascending (stride tb_selection_capacity() =
+ * min(ctx_cap, (2r+1) B + n_sink + n_local)).  If topb_idx is not NULL it
+ * receives T ascending with stride B (its count is min(B, hi - lo)).  If
  * sel_bits is not NULL it receives S as a bitmap (all tb_bitmap_words()
  * words of the head are written; bits at positions >= n are zero).  At
  * least one of sel_idx and sel_bits must be given.
@@ -189,6 +195,22 @@ int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
                    const int32_t *sel_count, const uint32_t *sel_bits, const int32_t *keep_from,
                    const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
                    size_t ws_bytes, void *stream);
+
+/*
+ * tb_dense_attn -- dense decode attention over the whole context, the
+ * baseline that TokenButler's speedups are measured against ([RES]: the
+ * on-GPU and CPU-offloading latency comparisons with dense attention).
+ *
+ * For query head h (KV head g = h*Hkv/Hq) of sequence b with n = ctx_len[b],
+ *   out[b][h] = sum_{t < n} softmax_t(scale * q[b][h] . K[b][g][t]) V[b][g][t],
+ * accumulated in fp32 and rounded to the dtype; n = 0 gives a zero row.
+ * Layouts as for tb_sparse_attn.  Every K/V row is read once and serves all
+ * query heads of its KV head.  The workspace holds the per-chunk partials.
+ * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ */
+int tb_dense_attn(const tb_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
+                  size_t ws_bytes, void *stream);
 
 /* Arguments of one fused decode step (all pointers device pointers). */
 typedef struct tb_step_args {

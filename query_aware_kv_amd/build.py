@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtokenbutler.so")
 
-SOURCES = ["tb_api.hip", "tb_project.hip", "tb_score.hip", "tb_select.hip", "tb_attn.hip"]
+SOURCES = ["tb_api.hip", "tb_project.hip", "tb_score.hip", "tb_select.hip", "tb_attn.hip",
+           "tb_dense.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

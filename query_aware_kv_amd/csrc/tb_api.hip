@@ -47,14 +47,13 @@ int check_params(const tb_select_params *p)
         return TB_EINVAL;
     if (p->budget <= 0 || p->radius < 0 || p->radius > 1024 || p->n_sink < 0 || p->n_local < 0)
         return TB_EINVAL;
-    if (p->n_sink != 0 || p->n_local != 0)
-        return TB_EUNSUPPORTED;
     return TB_OK;
 }
 
 int32_t sel_capacity(const tb_shape &s, const tb_select_params &p)
 {
-    const long long widened = (2LL * p.radius + 1) * (long long)p.budget;
+    const long long widened =
+        (2LL * p.radius + 1) * (long long)p.budget + (long long)p.n_sink + (long long)p.n_local;
     return (int32_t)(widened < s.ctx_cap ? widened : s.ctx_cap);
 }
 
@@ -205,6 +204,25 @@ int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
     return hip_rc(launch_attn(*shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count,
                               sel_bits, keep_from, ctx_len, softmax_scale, out, W.part_o,
                               W.part_ml, W.counters, (hipStream_t)stream));
+}
+
+int tb_dense_attn(const tb_shape *shape, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_shape(shape));
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || ctx_len == nullptr ||
+        out == nullptr)
+        return TB_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return TB_EINVAL;
+    if (!(softmax_scale == softmax_scale))
+        return TB_EINVAL;
+    WsLayout L;
+    TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    Ws W = carve(ws, L);
+    return hip_rc(launch_dense(*shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, W.part_o,
+                               W.part_ml, W.counters, (hipStream_t)stream));
 }
 
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,

@@ -30,36 +30,14 @@
 //      counter) merges the chunk partials -- max and weights first, then the
 //      weighted sums with all of its threads -- writes the output rows, and
 //      resets the counter to zero for the next call.
-#include "tb_internal.h"
+#include "tb_attn_common.h"
 
 namespace tb {
 namespace {
 
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kMaxChunks = kMaxCtxCap / kAttnChunk;
 constexpr int kRowsInFlight = 4; // rows per row slot loaded before use
-
-// Chunk partials cross work-groups (and XCDs, whose L2 caches are not
-// coherent with each other).  They are written and read with agent-scope
-// atomic accesses, which go through to the device coherence point, so no
-// full L2 write-back fence is needed to publish them.
-// Two 64-bit accesses per four floats: every agent-scope access is its own
-// memory transaction, so wider ones matter.
-__device__ __forceinline__ float4 load4_agent(const float *p)
-{
-    const double x = __hip_atomic_load(reinterpret_cast<const double *>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    const double y = __hip_atomic_load(reinterpret_cast<const double *>(p) + 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float2 lo = __builtin_bit_cast(float2, x), hi = __builtin_bit_cast(float2, y);
-    return make_float4(lo.x, lo.y, hi.x, hi.y);
-}
-__device__ __forceinline__ void store2_agent(float *p, float x, float y)
-{
-    __hip_atomic_store(reinterpret_cast<double *>(p), __builtin_bit_cast(double, make_float2(x, y)),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // First index e in [0, cnt] with L[e] >= v for an ascending list, found by
 // one wave; every lane returns the answer.
@@ -82,48 +60,6 @@ __device__ int wave_lower_bound(const int32_t *__restrict__ L, int cnt, int v)
     return lo + __popcll(__ballot(less));
 }
 
-// Sum of x over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32}); every
-// lane of the group receives the sum.  Within a 16-lane DPP row the partners
-// come from quad permutations and the half/full row mirrors.
-template <int N> __device__ __forceinline__ float group_sum(float x)
-{
-    if constexpr (N >= 2)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    if constexpr (N >= 4)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    if constexpr (N >= 8)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-    if constexpr (N >= 16)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-    if constexpr (N >= 32)
-        x += __shfl_xor(x, 16);
-    return x;
-}
-
-// Dot product of the 16-byte q and k pieces held by one lane.
-__device__ __forceinline__ float lane_dot_bf16(const uint4 &q, const uint4 &k)
-{
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    float d = 0.f;
-    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x),
-                                        __builtin_bit_cast(bf16x2, k.x), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y),
-                                        __builtin_bit_cast(bf16x2, k.y), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z),
-                                        __builtin_bit_cast(bf16x2, k.z), d, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w),
-                                        __builtin_bit_cast(bf16x2, k.w), d, false);
-    return d;
-}
-__device__ __forceinline__ float lane_dot_f32(const uint4 &q, const uint4 &k)
-{
-    float d = __uint_as_float(q.x) * __uint_as_float(k.x);
-    d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
-    d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
-    d = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
-    return d;
-}
-
 struct AttnArgs {
     const void *q, *k, *v;
     const int32_t *sel_idx;  // list mode
@@ -144,12 +80,6 @@ struct AttnArgs {
 template <typename T, int D, int GQ, bool BITMAP>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 {
-    auto lane_dot = [](const uint4 &qp, const uint4 &kp) -> float {
-        if constexpr (sizeof(T) == 2)
-            return lane_dot_bf16(qp, kp);
-        else
-            return lane_dot_f32(qp, kp);
-    };
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave step
@@ -163,16 +93,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     __shared__ uint32_t bm[GQ][NWD];
     __shared__ uint16_t hlist[kAttnWaves][PW]; // positions of each wave's part
     __shared__ uint32_t wcnt[kAttnWaves];
-    __shared__ uint32_t s_misc[4];
     __shared__ float mrg_m[GQ][NS];
     __shared__ float mrg_l[GQ][NS];
     __shared__ float mrg_f[GQ][NS];
     __shared__ float mrg_acc[GQ][NS][D];
     __shared__ float mrg_M[GQ], mrg_L[GQ];
-    __shared__ float cmb_f[GQ][kMaxChunks];
-    __shared__ float cmb_l[GQ][kMaxChunks];
-    __shared__ float cmb_ml[GQ][2];
-    __shared__ float4 red[kAttnThreads];
+    __shared__ CombineLds<GQ, kAttnThreads> cmb;
 
     const T *__restrict__ q = (const T *)a.q;
     const T *__restrict__ kc = (const T *)a.k;
@@ -323,7 +249,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
                 // logit in base 2, reduced over the row's lanes
-                const float z = group_sum<LPR>(lane_dot(qh, kk[r])) * a.qscale;
+                const float z = group_sum<LPR>(lane_dot<T>(qh, kk[r])) * a.qscale;
                 if (ok[r]) {
                     if (z > m) {
                         const float corr = __builtin_amdgcn_exp2f(m - z);
@@ -379,124 +305,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 #pragma unroll
             for (int s2 = 0; s2 < NS; ++s2)
                 O = fmaf(mrg_acc[h2][s2][dim], mrg_f[h2][s2], O);
-            const float M = mrg_M[h2], Ls = mrg_L[h2];
-            const size_t pc = (head0 + h2) * nchunk + c;
-            // even lanes store their own and the next lane's value (the
-            // next dimension of the same head) as one 64-bit access
-            const float On = __uint_as_float(dpp<0xB1>(__float_as_uint(O)));
-            if ((dim & 1) == 0)
-                store2_agent(&a.part_o[pc * D + dim], O, On);
-            if (dim == 0)
-                __hip_atomic_store(reinterpret_cast<double *>(a.part_ml) + pc,
-                                   __builtin_bit_cast(double, make_float2(M, Ls)),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            publish_partial<D>(a.part_o, a.part_ml, (head0 + h2) * nchunk + c, dim, O,
+                               mrg_M[h2], mrg_L[h2]);
         }
     }
 
     // ---- 5. arrival; the last work-group of this (b, g) merges the chunks ----
-    // The partial stores complete (vmcnt 0) before the counter moves; the
-    // signal fence keeps the compiler from sinking them below it.
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.counters[(size_t)b * a.Hkv + g], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_misc[1] = old == (uint32_t)(nchunk - 1) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_misc[1] == 0u)
-        return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const int nact = (n + kAttnChunk - 1) / kAttnChunk;
-    // Every load of the merge is issued up front: the chunk (max, sum) pairs
-    // into LDS, and each thread's weighted-sum inputs into registers.
-    constexpr int NCOL = GQ * D / 4;
-    constexpr int NPART = kAttnThreads / NCOL;
-    static_assert(NPART >= 1 && NPART * NCOL == kAttnThreads, "column split");
-    constexpr int PER = kMaxChunks / NPART; // chunks per thread at most
-    const int col = tid % NCOL, part = tid / NCOL;
-    const int chl = col / (D / 4), d4 = col % (D / 4);
-    for (int e = tid; e < GQ * nact; e += kAttnThreads) {
-        const int hl = e / nact, cc = e % nact;
-        const size_t pc = (head0 + hl) * nchunk + cc;
-        const double ml = __hip_atomic_load(reinterpret_cast<const double *>(a.part_ml) + pc,
-                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float2 v = __builtin_bit_cast(float2, ml);
-        cmb_f[hl][cc] = v.x;
-        cmb_l[hl][cc] = v.y;
-    }
-    const float *po = a.part_o + (head0 + chl) * nchunk * D + d4 * 4;
-    float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    // chunk weights need the maxima; the first batch of partial sums is
-    // loaded meanwhile
-    constexpr int BATCH = 8;
-    float4 v0[BATCH];
-#pragma unroll
-    for (int r = 0; r < BATCH; ++r) {
-        const int cc = part + r * NPART;
-        v0[r] = load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
-    }
-    __syncthreads();
-    for (int hl = wave; hl < GQ; hl += kAttnWaves) {
-        float M = -INFINITY;
-        for (int cc = lane; cc < nact; cc += 64)
-            M = fmaxf(M, cmb_f[hl][cc]);
-        M = wave_max(M);
-        float Ls = 0.f;
-        for (int cc = lane; cc < nact; cc += 64) {
-            const float mc = cmb_f[hl][cc];
-            const float f = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-            cmb_f[hl][cc] = f;
-            Ls = fmaf(cmb_l[hl][cc], f, Ls);
-        }
-        Ls = wave_sum(Ls);
-        if (lane == 0)
-            cmb_ml[hl][0] = Ls;
-    }
-    __syncthreads();
-    for (int c0b = part; c0b < nact; c0b += BATCH * NPART) {
-        float4 v[BATCH];
-#pragma unroll
-        for (int r = 0; r < BATCH; ++r) {
-            const int cc = c0b + r * NPART;
-            v[r] = c0b == part ? v0[r] : load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
-        }
-#pragma unroll
-        for (int r = 0; r < BATCH; ++r) {
-            const int cc = c0b + r * NPART;
-            const float f = cc < nact ? cmb_f[chl][cc] : 0.f;
-            s4.x = fmaf(v[r].x, f, s4.x);
-            s4.y = fmaf(v[r].y, f, s4.y);
-            s4.z = fmaf(v[r].z, f, s4.z);
-            s4.w = fmaf(v[r].w, f, s4.w);
-        }
-    }
-    red[part * NCOL + col] = s4;
-    (void)PER;
-    __syncthreads();
-    T *out = (T *)a.out;
-    for (int col = tid; col < NCOL; col += kAttnThreads) {
-        const int hl = col / (D / 4), d4 = col % (D / 4);
-        float4 s = red[col];
-        for (int p = 1; p < NPART; ++p) {
-            const float4 t = red[p * NCOL + col];
-            s.x += t.x;
-            s.y += t.y;
-            s.z += t.z;
-            s.w += t.w;
-        }
-        const float Ls = cmb_ml[hl][0];
-        const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
-        T *o = out + (head0 + hl) * D + d4 * 4;
-        o[0] = from_f32<T>(s.x * inv);
-        o[1] = from_f32<T>(s.y * inv);
-        o[2] = from_f32<T>(s.z * inv);
-        o[3] = from_f32<T>(s.w * inv);
-    }
-    if (tid == 0)
-        __hip_atomic_store(&a.counters[(size_t)b * a.Hkv + g], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    arrive_and_combine<T, D, GQ, kAttnThreads, kMaxChunks>(
+        cmb, &a.counters[(size_t)b * a.Hkv + g], a.part_o, a.part_ml, nchunk,
+        (n + kAttnChunk - 1) / kAttnChunk, head0, (T *)a.out);
 }
 
 template <typename T, int D, int GQ>

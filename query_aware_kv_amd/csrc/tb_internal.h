@@ -129,7 +129,8 @@ __device__ __forceinline__ float wave_sum(float x)
 }
 
 // ---------------------------------------------------------------- sizes
-constexpr int kAttnChunk = 1024;    // positions per attention work-group
+constexpr int kAttnChunk = 1024;    // positions per sparse attention work-group
+constexpr int kDenseChunk = 1024;   // positions per dense attention work-group
 constexpr int kMaxCtxCap = 262144;  // bounded by the selection kernel's LDS bitmaps
 constexpr size_t kAlign = 256;
 
@@ -147,6 +148,14 @@ struct WsLayout {
 inline int attn_chunks(int cap) { return (cap + kAttnChunk - 1) / kAttnChunk; }
 inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 
+inline int dense_chunks(int cap) { return (cap + kDenseChunk - 1) / kDenseChunk; }
+// Chunk partials are laid out per kernel's own chunk count; the region fits
+// the larger of the two.
+inline int max_chunks(int cap)
+{
+    return attn_chunks(cap) > dense_chunks(cap) ? attn_chunks(cap) : dense_chunks(cap);
+}
+
 inline WsLayout ws_layout(const tb_shape &s)
 {
     WsLayout L;
@@ -154,10 +163,10 @@ inline WsLayout ws_layout(const tb_shape &s)
     L.scores = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(float));
     L.part_o = off;
-    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * s.head_dim *
+    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * s.head_dim *
                     sizeof(float));
     L.part_ml = off;
-    off += align_up((size_t)s.batch * s.n_q_heads * attn_chunks(s.ctx_cap) * 2 * sizeof(float));
+    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * 2 * sizeof(float));
     L.counters = off;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
     L.total = off;
@@ -191,5 +200,10 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const int32_t *keep_from, const int32_t *ctx_len, float softmax_scale,
                        void *out, float *part_o, float *part_ml, uint32_t *counters,
                        hipStream_t st);
+
+hipError_t launch_dense(const tb_shape &s, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *ctx_len, float softmax_scale,
+                        void *out, float *part_o, float *part_ml, uint32_t *counters,
+                        hipStream_t st);
 
 } // namespace tb

@@ -30,6 +30,10 @@
 //   3. Every thread builds its own words of the kept set T from its keys; a
 //      block scan of per-word tie counts settles ties at tau by position.
 //   4. Dilation by r is word-wise shifts of the bitmap, clipped to [0, n).
+//      Inference Strategy (the three buffers): the sink [0, n_sink) and the
+//      local window (the last n_local positions) are always kept; only the
+//      positions between them compete for the budget (their keys are the
+//      only non-zero ones), and both ranges are ORed in after the dilation.
 //   5. A block scan of per-word popcounts gives |S| and, when the list is
 //      asked for, compacts the bitmap into the ascending index list; the
 //      bitmap itself can be written out too.
@@ -191,12 +195,14 @@ struct BinScan {
     }
 };
 
-// Loads the 32 keys of bitmap word w (positions >= n become key 0).  Whole
-// words of 16-byte aligned rows use four-float loads; a partial last word, or
-// a row whose start is not 16-byte aligned, is read one float at a time
-// without touching positions >= n.
-__device__ __forceinline__ void load_word_keys(const float *row, int w, int n, bool vec,
-                                               uint32_t (&k)[32])
+// Loads the 32 keys of bitmap word w.  Only positions in [lo, hi) (the
+// middle region between the sink and the local window, hi <= n) compete for
+// the budget; every other position gets key 0.  Whole words of 16-byte
+// aligned rows use four-float loads; a partial last word, or a row whose
+// start is not 16-byte aligned, is read one float at a time without touching
+// positions >= n.
+__device__ __forceinline__ void load_word_keys(const float *row, int w, int lo, int hi, int n,
+                                               bool vec, uint32_t (&k)[32])
 {
     const int p0 = w * 32;
     if (vec && p0 + 32 <= n) {
@@ -212,6 +218,11 @@ __device__ __forceinline__ void load_word_keys(const float *row, int w, int n, b
             k[4 * i + 2] = score_key(v[i].z);
             k[4 * i + 3] = score_key(v[i].w);
         }
+        if (p0 < lo || p0 + 32 > hi) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                k[e] = p0 + e >= lo && p0 + e < hi ? k[e] : 0u;
+        }
     } else {
         float f[32];
 #pragma unroll
@@ -219,8 +230,15 @@ __device__ __forceinline__ void load_word_keys(const float *row, int w, int n, b
             f[e] = row[p0 + e < n ? p0 + e : 0];
 #pragma unroll
         for (int e = 0; e < 32; ++e)
-            k[e] = p0 + e < n ? score_key(f[e]) : 0u;
+            k[e] = p0 + e >= lo && p0 + e < hi ? score_key(f[e]) : 0u;
     }
+}
+
+// Bits of word w for the positions p < x.
+__device__ __forceinline__ uint32_t mask_below(int w, int x)
+{
+    const int c = x - 32 * w;
+    return c <= 0 ? 0u : (c >= 32 ? 0xFFFFFFFFu : (1u << c) - 1u);
 }
 
 template <int WPT>
@@ -228,7 +246,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
     int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
-    uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new)
+    uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new,
+    int n_sink, int n_local)
 {
     extern __shared__ __align__(16) uint32_t lds[];
     uint32_t *hist = lds;                         // [kCopies][kCopyStride]
@@ -260,12 +279,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int nw = (n + 31) >> 5;
     const int nwt = (nw + kSelThreads - 1) / kSelThreads; // words per thread
     const bool vec = (cap & 3) == 0; // every row starts 16-byte aligned
+    // the sink [0, lo) and the local window [hi, n) are kept outright; the
+    // budget goes to the middle region [lo, hi)
+    const int lo = n_sink < n ? n_sink : n;
+    const int hi = n_local < n - lo ? n - n_local : lo;
     if (tid < 64)
         misc[tid] = 0u;
 
     uint32_t keys[32];
     if constexpr (WPT > 0)
-        load_word_keys(row, tid, n, vec, keys);
+        load_word_keys(row, tid, lo, hi, n, vec, keys);
     // fn(w, k) over this thread's words, k[e] the key of position 32w + e
     auto for_words = [&](auto &&fn) {
         if constexpr (WPT > 0) {
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         } else {
             for (int j = 0; j < nwt; ++j) {
                 uint32_t k[32];
-                load_word_keys(row, tid + j * kSelThreads, n, vec, k);
+                load_word_keys(row, tid + j * kSelThreads, lo, hi, n, vec, k);
                 fn(tid + j * kSelThreads, k);
             }
         }
@@ -318,7 +341,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         __syncthreads();
     };
 
-    const bool take_all = B >= n;
+    const bool take_all = B >= hi - lo;
     uint32_t tau = 0u, fmask = 0xFFFFFFFFu, need = 0u, cnt_eq = 0u;
     bool emitted = false; // Tb / Sb already hold the kept and tie bits
     if (!take_all) {
@@ -351,8 +374,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                         f[q] = row[p < n ? p : 0];
                     }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        s4[q] = p0 + 8 * q < n ? score_key(f[q]) : 0u;
+                    for (int q = 0; q < 4; ++q) {
+                        const int p = p0 + 8 * q;
+                        s4[q] = p >= lo && p < hi ? score_key(f[q]) : 0u;
+                    }
                 }
             };
             const int nsw = WPT > 0 ? 1 : nwt; // words sampled per thread
@@ -368,7 +393,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             if (wave == 0) {
                 // sample ranks a margin either side of the expected rank of tau
                 const BinScan sc(shist, lane);
-                const float pb = (float)B / (float)n;
+                const float pb = (float)B / (float)(hi - lo);
                 const float tr = pb * (float)sc.total;
                 const float mg = 4.5f * sqrtf((float)sc.total * pb * (1.f - pb)) + 3.f;
                 const int hi_rank = (int)floorf(tr - mg);
@@ -606,7 +631,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
 
     // ---- neighbor fetching: dilate T by r within [0, n) ----
-    const uint32_t *fin = Tb;
+    uint32_t *fin = Tb;
     if (r > 0) {
         const uint32_t *src = Tb;
         uint32_t *dst = Sb;
@@ -630,6 +655,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             src = dst;
             dst = (dst == Sb) ? Xb : Sb;
         }
+    }
+
+    // ---- the sink and the local window join the set ----
+    if (lo > 0 || hi < n) {
+        for (int w = tid; w < nw; w += kSelThreads)
+            fin[w] |= mask_below(w, lo) | (mask_below(w, n) & ~mask_below(w, hi));
+        __syncthreads();
     }
 
     // ---- |S|, the ascending list (when asked) and the bitmap (when asked) ----
@@ -667,7 +699,7 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
     hipLaunchKernelGGL(select_kernel<WPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
                        s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx, sel_stride,
                        sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap), keep_from,
-                       n_new);
+                       n_new, p.n_sink, p.n_local);
     return hipGetLastError();
 }
 

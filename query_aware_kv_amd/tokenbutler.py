@@ -74,10 +74,12 @@ def lib() -> ctypes.CDLL:
                                 ctypes.c_size_t, _vp]
         L.tb_sparse_attn.argtypes = [P(Shape), _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp,
                                      ctypes.c_float, _vp, _vp, ctypes.c_size_t, _vp]
+        L.tb_dense_attn.argtypes = [P(Shape), _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                    ctypes.c_size_t, _vp]
         L.tb_decode_step.argtypes = [P(Shape), P(SelectParams), P(StepArgs), _vp,
                                      ctypes.c_size_t, _vp]
         for fn in ("tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn",
-                   "tb_decode_step"):
+                   "tb_dense_attn", "tb_decode_step"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -217,6 +219,21 @@ def sparse_attn(shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count, keep
     _check("tb_sparse_attn", lib().tb_sparse_attn(
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx),
         int(sel_stride), _ptr(sel_count), _ptr(sel_bits), _ptr(keep_from), _ptr(ctx_len),
+        float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(stream)))
+
+
+def dense_attn(shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, ws, stream=None):
+    """Dense attention over every cached token [0, ctx_len)."""
+    e = _elt(shape)
+    qn = shape.batch * shape.n_q_heads * shape.head_dim
+    _expect("q", q, qn, e)
+    _expect("out", out, qn, e)
+    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("ctx_len", ctx_len, shape.batch, torch.int32)
+    _check("tb_dense_attn", lib().tb_dense_attn(
+        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
         float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
 

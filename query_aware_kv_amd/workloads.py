@@ -38,6 +38,8 @@ class Workload:
     plant_run_len: int    # ... of this length
     plant_shift: float    # score shift of a planted token, in score std units
     seed: int
+    n_sink: int = 0       # first tokens always kept (sink buffer)
+    n_local: int = 0      # last tokens always kept (local window)
 
     @property
     def ctx(self) -> int:
@@ -54,7 +56,7 @@ class Workload:
 
     @property
     def cap_s(self) -> int:
-        return min(self.ctx_cap, (2 * self.radius + 1) * self.budget)
+        return min(self.ctx_cap, (2 * self.radius + 1) * self.budget + self.n_sink + self.n_local)
 
     @property
     def group(self) -> int:

@@ -61,7 +61,7 @@ def device_case(w: Workload, layer: int = 0, pre: synth.Prefill | None = None) -
     pre = pre if pre is not None else synth.prefill(w, layer)
     dev = "cuda"
     shape = shape_of(w)
-    params = tbl.make_params(w.budget, w.radius)
+    params = tbl.make_params(w.budget, w.radius, w.n_sink, w.n_local)
     cap_s = tbl.selection_capacity(shape, params)
     K = pre.K.to(dev)
     V = pre.V.to(dev)
@@ -103,7 +103,8 @@ def oracle_state(w: Workload, pre: synth.Prefill, b: int) -> orc.SequenceState:
     V = f64(pre.V[b])
     Kp = np.zeros((w.n_kv_heads, w.ctx_cap, w.d_imp))
     Kp[:, :w.ctx0] = orc.project(K[:, :w.ctx0], f64(pre.W), odtype(w))
-    return orc.SequenceState(K, V, Kp, Himp=w.n_imp_heads, B=w.budget, r=w.radius)
+    return orc.SequenceState(K, V, Kp, Himp=w.n_imp_heads, B=w.budget, r=w.radius,
+                             n_sink=w.n_sink, n_local=w.n_local)
 
 
 def oracle_step(w: Workload, st: orc.SequenceState, pre: synth.Prefill, inp: synth.StepInputs,

@@ -28,7 +28,7 @@ def _exported_symbols():
 
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
-    assert {"tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn",
+    assert {"tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn", "tb_dense_attn",
             "tb_decode_step"} <= set(declared)
     exported = _exported_symbols()
     missing = [f for f in declared if f not in exported]
@@ -61,6 +61,9 @@ def test_workspace_and_capacity():
     assert tbl.selection_capacity(s, p) == 3277
     assert tbl.selection_capacity(s, tbl.make_params(3277, 1)) == 3 * 3277
     assert tbl.selection_capacity(_shape(ctx_cap=1000), tbl.make_params(600, 2)) == 1000
+    # the sink and the local window add their sizes
+    assert tbl.selection_capacity(s, tbl.make_params(3277, 1, n_sink=4, n_local=64)) == \
+        3 * 3277 + 68
     assert tbl.bitmap_words(_shape(ctx_cap=1000)) == 32
     assert tbl.bitmap_words(_shape(ctx_cap=1024)) == 32
     assert tbl.workspace_bytes(_shape(head_dim=96), p) == 0
@@ -95,8 +98,10 @@ def test_null_pointers_and_params_rejected():
                        fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, -1)), fake, fake, fake,
                        fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
-    assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, 1, n_sink=4)), fake,
-                       fake, fake, fake, None, None, fake, 1 << 30, None) == tbl.TB_EUNSUPPORTED
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, 1, n_sink=-1)), fake,
+                       fake, fake, fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
+    assert L.tb_select(ctypes.byref(s), ctypes.byref(tbl.make_params(5, 1, n_local=-3)), fake,
+                       fake, fake, fake, None, None, fake, 1 << 30, None) == tbl.TB_EINVAL
     assert L.tb_project_keys(ctypes.byref(s), fake, fake, fake, -1, fake, None) == tbl.TB_EINVAL
     assert L.tb_project_keys(ctypes.byref(s), fake, fake, None, 4, fake, None) == tbl.TB_EINVAL
     # n_tokens == 0 is a no-op that launches nothing
@@ -127,6 +132,28 @@ def test_workspace_checks():
     # scores are read in 16-byte pieces
     assert L.tb_select(ctypes.byref(s), ctypes.byref(p), ctypes.c_void_p((1 << 20) + 4), fake,
                        fake, fake, None, None, fake, need, None) == tbl.TB_EINVAL
+
+
+def test_dense_attn_argument_checks():
+    L = tbl.lib()
+    s = _shape()
+    need = tbl.workspace_bytes(s, tbl.make_params(100, 1))
+    fake = ctypes.c_void_p(1 << 20)
+    misaligned = ctypes.c_void_p((1 << 20) + 2)
+    scale = ctypes.c_float(0.1)
+    assert L.tb_dense_attn(ctypes.byref(s), None, fake, fake, fake, scale, fake, fake, need,
+                           None) == tbl.TB_EINVAL
+    assert L.tb_dense_attn(ctypes.byref(s), fake, fake, fake, None, scale, fake, fake, need,
+                           None) == tbl.TB_EINVAL
+    assert L.tb_dense_attn(ctypes.byref(s), fake, misaligned, fake, fake, scale, fake, fake,
+                           need, None) == tbl.TB_EINVAL
+    assert L.tb_dense_attn(ctypes.byref(s), fake, fake, fake, fake, ctypes.c_float(float("nan")),
+                           fake, fake, need, None) == tbl.TB_EINVAL
+    assert L.tb_dense_attn(ctypes.byref(s), fake, fake, fake, fake, scale, fake, fake, need - 1,
+                           None) == tbl.TB_EWORKSPACE
+    bad = _shape(head_dim=96)
+    assert L.tb_dense_attn(ctypes.byref(bad), fake, fake, fake, fake, scale, fake, fake, need,
+                           None) == tbl.TB_EUNSUPPORTED
 
 
 def test_decode_step_argument_checks():

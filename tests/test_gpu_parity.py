@@ -171,9 +171,13 @@ def test_batched_32_layer_workload_sampled(layer):
     assert cnt.max() <= 3 * w.budget and cnt.min() >= w.budget
 
 
-def test_prediction_interval_run():
-    # 64 steps, selection recomputed every 8 steps, radius 2, new tokens kept
-    w = INTERVAL_16K
+@pytest.mark.parametrize("w", [INTERVAL_16K,
+                               replace(INTERVAL_16K, name="interval_sink_local", steps=20,
+                                       n_sink=4, n_local=256)],
+                         ids=lambda w: w.name)
+def test_prediction_interval_run(w):
+    # selection recomputed every 8 steps, radius 2, new tokens kept (64
+    # steps; 20 with a sink and a local window)
     dc = device_case(w)
     check = (0, 3)
     states = {b: oracle_state(w, dc.pre, b) for b in check}
@@ -216,7 +220,11 @@ def _small(**kw) -> Workload:
     dict(budget=3000),                                # budget >= context: dense
     dict(radius=40),                                  # dilation in several passes
     dict(n_q_heads=2, n_kv_heads=2, n_imp_heads=2, head_dim=64),
-], ids=["base", "f32", "imp_per_kv", "group8", "B1", "dense", "r40", "mha_d64"])
+    dict(n_sink=4, n_local=64),                       # sink and local window
+    dict(n_sink=800, n_local=1500, budget=20),        # the buffers cover every context
+    dict(n_sink=3, n_local=5, radius=2, dtype="f32", head_dim=64, d_imp=16),
+], ids=["base", "f32", "imp_per_kv", "group8", "B1", "dense", "r40", "mha_d64", "sink_local",
+        "buffers_cover", "sink_local_f32"])
 def test_ragged_batch_fused(kw):
     # three sequences of different lengths (1, 700 and 2000 tokens) in one launch
     w = _small(**kw)
@@ -249,11 +257,11 @@ def test_ragged_batch_fused(kw):
                 assert np.abs(f64(out[b, h]) - dense).max() <= TOL[w.dtype]
 
 
-def _select_case(scores_rows, lens, B, r):
+def _select_case(scores_rows, lens, B, r, n_sink=0, n_local=0):
     """tb_select on crafted fp32 scores [b][H][cap]."""
     bsz, H, cap = scores_rows.shape
     shape = tbl.make_shape(bsz, H, H, H, 64, 16, cap, torch.float32)
-    params = tbl.make_params(B, r)
+    params = tbl.make_params(B, r, n_sink, n_local)
     cap_s = tbl.selection_capacity(shape, params)
     ws = tbl.alloc_workspace(shape, params)
     sc = torch.from_numpy(np.ascontiguousarray(scores_rows, dtype=np.float32)).cuda()
@@ -274,9 +282,9 @@ def _select_case(scores_rows, lens, B, r):
         got = lists_of(sel, cnt, b)
         got_bits = bitmap_positions(bits, b, n)
         for i in range(H):
-            T_ref = orc.topb(scores_rows[b, i, :n], B)
+            T_ref, S_ref = orc.select(scores_rows[b, i, :n], B, r, n_sink, n_local)
             assert topb[b, i, :T_ref.size].cpu().tolist() == T_ref.tolist(), (b, i)
-            assert got[i] == orc.expand(T_ref, n, r).tolist(), (b, i)
+            assert got[i] == S_ref.tolist(), (b, i)
             assert got_bits[i] == got[i], (b, i)
 
 
@@ -322,6 +330,30 @@ def test_select_long_rows(kind, cap, lens):
     rows = _long_rows(kind, len(lens), 2, cap, seed=cap + len(kind))
     for B, r in [(max(lens) // 10, 1), (1, 0), (lens[-1] - 1, 0), (4000, 2)]:
         _select_case(rows, lens, B, r)
+
+
+@pytest.mark.parametrize("kind", ["gauss", "levels", "equal"])
+@pytest.mark.parametrize("cap,lens", [(32768, [32768, 20001, 2049]), (70000, [70000, 40000])])
+def test_select_long_rows_sink_and_window(kind, cap, lens):
+    # the sink and the local window are kept outright and the budget goes to
+    # the positions between them (ranges that end inside bitmap words)
+    rows = _long_rows(kind, len(lens), 2, cap, seed=cap + 3 * len(kind))
+    for B, r, ns, nl in [(max(lens) // 10, 1, 7, 1000), (1, 0, 4, 1), (2000, 2, 33, 4095),
+                         (lens[-1], 0, 100, 100), (500, 0, 0, 64), (500, 1, 64, 0)]:
+        _select_case(rows, lens, B, r, ns, nl)
+
+
+@pytest.mark.parametrize("B,r", [(1, 0), (37, 1), (700, 0)])
+def test_select_sink_and_window_crafted(B, r):
+    rng = np.random.default_rng(B * 10 + r)
+    cap = 1500
+    rows = np.empty((3, 4, cap), dtype=np.float32)
+    rows[:, 0] = rng.standard_normal((3, cap))
+    rows[:, 1] = rng.integers(-3, 4, size=(3, cap))
+    rows[:, 2] = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), size=(3, cap))
+    rows[:, 3] = 2.5
+    for ns, nl in [(4, 16), (0, 300), (900, 0), (800, 800), (1, 1499), (3000, 0)]:
+        _select_case(rows, [1, 777, 1500], B, r, ns, nl)
 
 
 def test_select_many_rows_reused_workspace():
