@@ -53,6 +53,8 @@ def _load():
         lib.orc_topb.restype = i32
         lib.orc_expand.argtypes = [P, i32, i32, i32, P]
         lib.orc_expand.restype = i32
+        lib.orc_mlp.argtypes = [P, P, P] + [ctypes.c_int] * 8 + [P]
+        lib.orc_mlp.restype = None
         lib.orc_buffers.argtypes = [i32, i32, i32, P, P]
         lib.orc_buffers.restype = None
         lib.orc_select.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
@@ -147,6 +149,23 @@ def attend(q, K, V, S, scale: float, return_weights: bool = False):
     _load().orc_attend(_p(q), _p(K), _p(V), D, _p(S), S.size, float(scale), _p(out), _p(w))
     if return_weights:
         return out, w[:S.size].copy()
+    return out
+
+
+ACT_RELU = 0
+ACT_SILU = 1
+
+
+def mlp(h, W1, W2, G: int, Himp: int, d: int, act: int, dtype: int) -> np.ndarray:
+    """Importance queries from hidden states h [M, E] through the two-layer
+    MLP (W1 [F, E], W2 [G*Himp*d, F], output-major, no biases); returns
+    q_imp [G, M, Himp, d] rounded to the dtype."""
+    h, W1, W2 = _f64(h), _f64(W1), _f64(W2)
+    M, E = h.shape
+    F = W1.shape[0]
+    assert W1.shape == (F, E) and W2.shape == (G * Himp * d, F)
+    out = np.empty((G, M, Himp, d), dtype=np.float64)
+    _load().orc_mlp(_p(h), _p(W1), _p(W2), M, E, F, G, Himp, d, int(act), int(dtype), _p(out))
     return out
 
 

@@ -211,6 +211,51 @@ int32_t orc_expand(const int32_t *T, int32_t nT, int32_t n, int32_t r, int32_t *
 }
 
 /* ------------------------------------------------------------------ */
+/* Importance-query producer ([ARCH] Query Prediction)                 */
+/* ------------------------------------------------------------------ */
+
+#define ORC_ACT_RELU 0
+#define ORC_ACT_SILU 1
+
+static double orc_act(double x, int act)
+{
+    if (act == ORC_ACT_SILU)
+        return x / (1.0 + exp(-x));
+    return x > 0.0 ? x : 0.0;
+}
+
+/*
+ * The lightweight MLP on the producer layer's hidden states:
+ *   u[m][f] = round_dtype( act( sum_e h[m][e] * W1[f][e] ) )      (fp64 sum)
+ *   y[m][n] = round_dtype( sum_f u[m][f] * W2[n][f] )             (fp64 sum)
+ * with n = (g * Himp + i) * d + j, written slot-major:
+ *   q_imp[g][m][i][j] = y[m][n],  G = N / (Himp * d) slots.
+ * Weights are stored output-major ([F][E] and [N][F]).  No biases.
+ */
+void orc_mlp(const double *h, const double *W1, const double *W2, int M, int E, int F, int G,
+             int Himp, int d, int act, int dtype, double *q_imp)
+{
+    const int N = G * Himp * d;
+    double *u = (double *)malloc((size_t)M * F * sizeof(double));
+    for (int m = 0; m < M; ++m)
+        for (int f = 0; f < F; ++f) {
+            double acc = 0.0;
+            for (int e = 0; e < E; ++e)
+                acc += h[(int64_t)m * E + e] * W1[(int64_t)f * E + e];
+            u[(int64_t)m * F + f] = round_to_dtype(orc_act(acc, act), dtype);
+        }
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int f = 0; f < F; ++f)
+                acc += u[(int64_t)m * F + f] * W2[(int64_t)n * F + f];
+            const int g = n / (Himp * d), r = n % (Himp * d);
+            q_imp[((int64_t)g * M + m) * Himp * d + r] = round_to_dtype(acc, dtype);
+        }
+    free(u);
+}
+
+/* ------------------------------------------------------------------ */
 /* The three buffers ([INF]: sink, local window, important)            */
 /* ------------------------------------------------------------------ */
 

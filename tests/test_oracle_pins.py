@@ -279,6 +279,94 @@ def test_expand_golden_hand_cases():
 
 
 # --------------------------------------------------------------------------
+# importance-query producer (two-layer MLP)
+# --------------------------------------------------------------------------
+
+def _rne_fraction(x: Fraction, bits: int) -> Fraction:
+    """x rounded to `bits` significant bits, ties to even (no range limits)."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    scaled = a * 2 ** (bits - 1)
+    fl = scaled.numerator // scaled.denominator
+    rem = scaled - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * Fraction(fl) / 2 ** (bits - 1) * Fraction(2) ** e
+
+
+def _mlp_exact(h, W1, W2, G, Himp, d, bits):
+    # independent formulation: exact rational arithmetic, ReLU, rounding to
+    # `bits` significant bits after the activation and at the output
+    M, E = h.shape
+    F = W1.shape[0]
+    N = G * Himp * d
+    u = [[_rne_fraction(max(Fraction(0), sum(Fraction(int(h[m, e])) * int(W1[f, e])
+                                             for e in range(E))), bits)
+          for f in range(F)] for m in range(M)]
+    out = np.zeros((G, M, Himp, d))
+    for m in range(M):
+        for n in range(N):
+            y = _rne_fraction(sum(u[m][f] * int(W2[n, f]) for f in range(F)), bits)
+            g, rest = divmod(n, Himp * d)
+            i, j = divmod(rest, d)
+            out[g, m, i, j] = float(y)
+    return out
+
+
+@pytest.mark.parametrize("dtype,bits,scale", [(orc.F32, 24, 3), (orc.BF16, 8, 3),
+                                              (orc.BF16, 8, 100)])
+def test_mlp_exact_integers(dtype, bits, scale):
+    rng = np.random.default_rng(500 + scale)
+    M, E, F, G, Himp, d = 3, 8, 6, 2, 2, 3
+    h = rng.integers(-scale, scale + 1, size=(M, E)).astype(np.float64)
+    W1 = rng.integers(-3, 4, size=(F, E)).astype(np.float64)
+    W2 = rng.integers(-3, 4, size=(G * Himp * d, F)).astype(np.float64)
+    got = orc.mlp(h, W1, W2, G, Himp, d, orc.ACT_RELU, dtype)
+    np.testing.assert_array_equal(got, _mlp_exact(h, W1, W2, G, Himp, d, bits))
+    if scale == 100:   # some hidden values need more than 8 bits: rounding matters
+        pre = np.maximum(h @ W1.T, 0)
+        assert any(_rne_fraction(Fraction(int(v)), 8) != int(v) for v in pre.ravel())
+
+
+def test_mlp_activation_closed_forms():
+    one = np.ones((1, 1))
+    # SiLU(1) = 1 / (1 + e^-1), rounded once to fp32 (hidden), then times 1
+    y = orc.mlp(one, one, one, 1, 1, 1, orc.ACT_SILU, orc.F32)
+    assert y[0, 0, 0, 0] == float(np.float32(1.0 / (1.0 + math.exp(-1.0))))
+    # SiLU(-2) = -2 / (1 + e^2)
+    y = orc.mlp(one, -2 * one, one, 1, 1, 1, orc.ACT_SILU, orc.F32)
+    assert y[0, 0, 0, 0] == float(np.float32(-2.0 / (1.0 + math.exp(2.0))))
+    # ReLU clips a negative pre-activation to zero
+    y = orc.mlp(one, -one, one, 1, 1, 1, orc.ACT_RELU, orc.F32)
+    assert y[0, 0, 0, 0] == 0.0
+
+
+def test_mlp_slot_major_layout():
+    # W2 row n copies hidden unit n, so q_imp[g][m][i][j] must equal the
+    # hidden unit n = (g * Himp + i) * d + j of token m
+    M, G, Himp, d = 2, 3, 2, 2
+    N = G * Himp * d
+    h = np.arange(1, M * N + 1, dtype=np.float64).reshape(M, N)
+    W1 = np.eye(N)
+    W2 = np.eye(N)
+    q = orc.mlp(h, W1, W2, G, Himp, d, orc.ACT_RELU, orc.F32)
+    for g in range(G):
+        for m in range(M):
+            for i in range(Himp):
+                for j in range(d):
+                    assert q[g, m, i, j] == h[m, (g * Himp + i) * d + j]
+
+
+# --------------------------------------------------------------------------
 # sink, local window and important buffer
 # --------------------------------------------------------------------------
 
