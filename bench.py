@@ -14,6 +14,7 @@ Prints one JSON line.  Extra legs:
                 with HIP events on its stream over K launches, against 8 TB/s;
   dense_attention  the dense decode-attention kernel over the whole context at
                 the same shape (the baseline of the pages' speedup claims);
+  predictor_mlp the importance-query producer MLP (weight-streaming bound);
   cpu_baseline  the fp64 C oracle's decode step on the host (1 thread), on a
                 bounded number of steps.
 """
@@ -207,6 +208,28 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_dense = e0.elapsed_time(e1) / a.steps
 
+    # the importance-query producer MLP at the step's batch: Llama-3-8B hidden
+    # size, inner width 1024, four consumer slots of this shape's heads
+    mshape = tbl.make_mlp_shape(w.batch, 4096, 1024, 4, w.n_imp_heads, w.d_imp, q.dtype,
+                                tbl.TB_ACT_SILU)
+    n_out = 4 * w.n_imp_heads * w.d_imp
+    mins = [synth.mlp_inputs(w.batch, 4096, 1024, n_out, q.dtype, 40 + r) for r in range(R)]
+    mdev = [(m.h.to(dev), m.w1.to(dev), m.w2.to(dev)) for m in mins]
+    mws = tbl.alloc_mlp_workspace(mshape, dev)
+    q_pred = torch.empty((4, w.batch, w.n_imp_heads, w.d_imp), dtype=q.dtype, device=dev)
+    for s in range(a.warmup):
+        tbl.predict_queries(mshape, *mdev[s % R], q_pred, mws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(a.steps):
+        tbl.predict_queries(mshape, *mdev[s % R], q_pred, mws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_mlp = e0.elapsed_time(e1) / a.steps
+    mlp_bytes = (4096 * 1024 + 1024 * n_out) * w.elt_bytes
+    mlp_gbs = mlp_bytes / (ms_mlp * 1e-3) / 1e9
+    log(f"bench: importance-query MLP {ms_mlp * 1e3:.2f} us, {mlp_gbs:.0f} GB/s")
+
     uniq, logical = unique_rows(reps[0]["bits"], w, w.ctx)
     row_bytes = w.head_dim * w.elt_bytes
     gather_bytes = uniq * 2 * row_bytes
@@ -263,6 +286,11 @@ def main() -> int:
                             "algorithmic_bytes": dense_bytes, "achieved": dense_gbs,
                             "frac": dense_gbs / PEAK_HBM_GBS,
                             "speedup_of_sparse_step": ms_dense / ms_step},
+        "predictor_mlp": {"kernel": "mlp_layer_kernel x2 (tb_predict_queries)",
+                          "shape": {"tokens": w.batch, "hidden": 4096, "inner": 1024,
+                                    "slots": 4, "imp_heads": w.n_imp_heads, "d_imp": w.d_imp},
+                          "us_per_call": ms_mlp * 1e3, "algorithmic_bytes": mlp_bytes,
+                          "achieved": mlp_gbs, "frac": mlp_gbs / PEAK_HBM_GBS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -212,6 +212,44 @@ int tb_dense_attn(const tb_shape *shape, const void *q, const void *k_cache, con
                   const int32_t *ctx_len, float softmax_scale, void *out, void *ws,
                   size_t ws_bytes, void *stream);
 
+/*
+ * The importance-query producer ([ARCH] Query Prediction): a lightweight MLP
+ * maps the hidden states of a producer layer to G slot-specific importance
+ * queries per importance head, one slot per consumer layer it serves.
+ */
+#define TB_ACT_RELU 0
+#define TB_ACT_SILU 1
+
+typedef struct tb_mlp_shape {
+    int32_t tokens;      /* M: hidden-state rows (sequences in a decode step), 1 .. 64 */
+    int32_t hidden;      /* E: producer hidden size, a multiple of 256 */
+    int32_t inner;       /* F: MLP inner width, a multiple of 256 */
+    int32_t n_slots;     /* G: query slots (consumer layers served), >= 1 */
+    int32_t n_imp_heads; /* Himp: importance heads of each consumer layer */
+    int32_t d_imp;       /* d: importance dimension; G*Himp*d a multiple of 64 */
+    int32_t dtype;       /* TB_F32 or TB_BF16 (inputs, weights, hidden layer, output) */
+    int32_t act;         /* TB_ACT_RELU or TB_ACT_SILU */
+} tb_mlp_shape;
+
+/* Workspace bytes of tb_predict_queries (0 if the shape is invalid). */
+size_t tb_mlp_workspace_bytes(const tb_mlp_shape *shape);
+
+/*
+ * tb_predict_queries -- importance queries from hidden states.
+ *   u[m][f] = round( act( sum_e h[m][e] * w1[f][e] ) )
+ *   q_imp[g][m][i][j] = round( sum_f u[m][f] * w2[(g*Himp + i)*d + j][f] )
+ * h [M][E], w1 [F][E], w2 [G*Himp*d][F] (output-major, like a linear
+ * layer's weight), q_imp [G][M][Himp][d]: slot g is the q_imp argument of
+ * tb_score / tb_decode_step for its consumer layer (batch = M).  No biases.
+ * Products are accumulated in fp32 on the matrix cores; round() is to the
+ * dtype, nearest even.  h, w1, w2 16-byte aligned; the workspace (at least
+ * tb_mlp_workspace_bytes(), 256-byte aligned, zero-filled before first use)
+ * holds the hidden layer and split-K partials and is left reusable.
+ * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE, TB_EHIP.
+ */
+int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1, const void *w2,
+                       void *q_imp, void *ws, size_t ws_bytes, void *stream);
+
 /* Arguments of one fused decode step (all pointers device pointers). */
 typedef struct tb_step_args {
     const void *q;        /* [b][Hq][D] */

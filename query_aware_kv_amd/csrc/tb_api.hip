@@ -84,6 +84,24 @@ int check_ws(const tb_shape &s, void *ws, size_t ws_bytes, WsLayout *L)
     return TB_OK;
 }
 
+int check_mlp(const tb_mlp_shape *s)
+{
+    if (s == nullptr)
+        return TB_EINVAL;
+    if (s->tokens <= 0 || s->hidden <= 0 || s->inner <= 0 || s->n_slots <= 0 ||
+        s->n_imp_heads <= 0 || s->d_imp <= 0)
+        return TB_EINVAL;
+    if (s->dtype != TB_F32 && s->dtype != TB_BF16)
+        return TB_EUNSUPPORTED;
+    if (s->act != TB_ACT_RELU && s->act != TB_ACT_SILU)
+        return TB_EUNSUPPORTED;
+    const long long N = (long long)s->n_slots * s->n_imp_heads * s->d_imp;
+    if (s->tokens > 64 || s->hidden % kMlpKGrain != 0 || s->inner % kMlpKGrain != 0 ||
+        N % 64 != 0 || N > (1LL << 20) || s->hidden > (1 << 20) || s->inner > (1 << 20))
+        return TB_EUNSUPPORTED;
+    return TB_OK;
+}
+
 #define TB_TRY(x)                                                                                  \
     do {                                                                                           \
         const int rc_ = (x);                                                                       \
@@ -102,7 +120,7 @@ const char *tb_strerror(int code)
     switch (code) {
     case TB_OK: return "ok";
     case TB_EINVAL: return "invalid argument (null pointer, bad size, misaligned pointer or inconsistent head counts)";
-    case TB_EUNSUPPORTED: return "unsupported dtype, head_dim, d_imp, group size, ctx_cap or reserved parameter";
+    case TB_EUNSUPPORTED: return "unsupported dtype, head_dim, d_imp, group size, ctx_cap, activation or MLP size";
     case TB_EWORKSPACE: return "workspace smaller than tb_workspace_bytes()";
     case TB_EHIP: return "HIP kernel launch failed";
     }
@@ -223,6 +241,28 @@ int tb_dense_attn(const tb_shape *shape, const void *q, const void *k_cache, con
     Ws W = carve(ws, L);
     return hip_rc(launch_dense(*shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, W.part_o,
                                W.part_ml, W.counters, (hipStream_t)stream));
+}
+
+size_t tb_mlp_workspace_bytes(const tb_mlp_shape *shape)
+{
+    if (check_mlp(shape) != TB_OK)
+        return 0;
+    return mlp_layout(*shape).total;
+}
+
+int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1, const void *w2,
+                       void *q_imp, void *ws, size_t ws_bytes, void *stream)
+{
+    TB_TRY(check_mlp(shape));
+    if (h == nullptr || w1 == nullptr || w2 == nullptr || q_imp == nullptr)
+        return TB_EINVAL;
+    if (!aligned16(h) || !aligned16(w1) || !aligned16(w2))
+        return TB_EINVAL;
+    if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0)
+        return TB_EINVAL;
+    if (ws_bytes < mlp_layout(*shape).total)
+        return TB_EWORKSPACE;
+    return hip_rc(launch_mlp(*shape, h, w1, w2, q_imp, ws, (hipStream_t)stream));
 }
 
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,

@@ -201,6 +201,19 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        void *out, float *part_o, float *part_ml, uint32_t *counters,
                        hipStream_t st);
 
+// Importance-query producer (tb_mlp.hip).  Workspace layout in bytes.
+constexpr int kMlpKGrain = 256; // k values per k-slice are a multiple of this
+struct MlpLayout {
+    size_t hidden;   // [M][F] hidden layer in the dtype
+    size_t part;     // split-K fp32 partials
+    size_t counters; // per 64-column block arrival counters (kept zero)
+    size_t total;
+};
+int mlp_k_slices(int K, int N);
+MlpLayout mlp_layout(const tb_mlp_shape &s);
+hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, const void *w2,
+                      void *q_imp, void *ws, hipStream_t st);
+
 hipError_t launch_dense(const tb_shape &s, const void *q, const void *k_cache,
                         const void *v_cache, const int32_t *ctx_len, float softmax_scale,
                         void *out, float *part_o, float *part_ml, uint32_t *counters,

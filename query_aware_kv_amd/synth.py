@@ -5,7 +5,8 @@ arithmetic and is shared, as data, by the GPU tests, the oracle checks and the
 benchmark.  Every tensor comes from its own numpy PCG64 stream keyed by
 ``[seed, tensor_id, layer, batch_item, slot]``:
 
-    tensor_id 0 K, 1 V, 2 q, 3 q_imp, 4 W, 5 planted positions
+    tensor_id 0 K, 1 V, 2 q, 3 q_imp, 4 W, 5 planted positions,
+              6 producer hidden states, 7 MLP W1, 8 MLP W2
     slot      0 for the prefill, s + 1 for decode step s (q, q_imp, new K/V),
               the importance-head index for planted positions
 
@@ -32,6 +33,7 @@ import torch
 from .workloads import Workload
 
 K_ID, V_ID, Q_ID, QIMP_ID, W_ID, PLANT_ID = 0, 1, 2, 3, 4, 5
+H_ID, W1_ID, W2_ID = 6, 7, 8
 
 
 def torch_dtype(w: Workload) -> torch.dtype:
@@ -165,3 +167,22 @@ def step_inputs(w: Workload, s: int, pre: Prefill, layer: int = 0) -> StepInputs
     q = draw_q(w, s, layer)
     q_imp = (pre.q_imp0 if s == 0 else draw_q_imp(w, s, layer)) if refresh else None
     return StepInputs(k_new=k_new, v_new=v_new, q=q, q_imp=q_imp, refresh=refresh)
+
+
+@dataclass
+class MlpInputs:
+    h: torch.Tensor   # [M][E] producer hidden states, N(0, 1)
+    w1: torch.Tensor  # [F][E], N(0, 1/E)
+    w2: torch.Tensor  # [N][F], N(0, 1/F)
+
+
+def mlp_inputs(M: int, E: int, F: int, N: int, dtype: torch.dtype, seed: int,
+               step: int = 0) -> MlpInputs:
+    """Random-init weights and hidden states of the importance-query MLP
+    (no trained weights exist here), rounded to the dtype."""
+    def draw(shape, tid, scale, slot=0):
+        z = np.random.default_rng([seed, tid, 0, 0, slot]).standard_normal(shape, dtype=np.float32)
+        a = z.astype(np.float64) * scale
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dtype)
+    return MlpInputs(h=draw((M, E), H_ID, 1.0, step + 1), w1=draw((F, E), W1_ID, 1 / np.sqrt(E)),
+                     w2=draw((N, F), W2_ID, 1 / np.sqrt(F)))

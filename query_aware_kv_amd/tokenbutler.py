@@ -28,6 +28,14 @@ class Shape(ctypes.Structure):
                 ("ctx_cap", _i32), ("dtype", _i32)]
 
 
+class MlpShape(ctypes.Structure):
+    _fields_ = [("tokens", _i32), ("hidden", _i32), ("inner", _i32), ("n_slots", _i32),
+                ("n_imp_heads", _i32), ("d_imp", _i32), ("dtype", _i32), ("act", _i32)]
+
+
+TB_ACT_RELU, TB_ACT_SILU = 0, 1
+
+
 class SelectParams(ctypes.Structure):
     _fields_ = [("budget", _i32), ("radius", _i32), ("n_sink", _i32), ("n_local", _i32)]
 
@@ -78,8 +86,12 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_size_t, _vp]
         L.tb_decode_step.argtypes = [P(Shape), P(SelectParams), P(StepArgs), _vp,
                                      ctypes.c_size_t, _vp]
+        L.tb_mlp_workspace_bytes.argtypes = [P(MlpShape)]
+        L.tb_mlp_workspace_bytes.restype = ctypes.c_size_t
+        L.tb_predict_queries.argtypes = [P(MlpShape), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                                         _vp]
         for fn in ("tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn",
-                   "tb_dense_attn", "tb_decode_step"):
+                   "tb_dense_attn", "tb_decode_step", "tb_predict_queries"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -236,6 +248,38 @@ def dense_attn(shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, ws, stre
         ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
         float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
+
+
+def make_mlp_shape(tokens, hidden, inner, n_slots, n_imp_heads, d_imp, dtype,
+                   act=TB_ACT_RELU) -> MlpShape:
+    code = {torch.float32: TB_F32, torch.bfloat16: TB_BF16}.get(dtype, dtype)
+    return MlpShape(tokens, hidden, inner, n_slots, n_imp_heads, d_imp, code, act)
+
+
+def mlp_workspace_bytes(shape: MlpShape) -> int:
+    return int(lib().tb_mlp_workspace_bytes(ctypes.byref(shape)))
+
+
+def alloc_mlp_workspace(shape: MlpShape, device="cuda"):
+    """A zero-filled workspace for tb_predict_queries."""
+    n = mlp_workspace_bytes(shape)
+    if n == 0:
+        raise ValueError("invalid MLP shape")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def predict_queries(shape: MlpShape, h, w1, w2, q_imp, ws, stream=None):
+    """Importance queries q_imp [G][M][Himp][d] from hidden states h [M][E]
+    through the two-layer MLP w1 [F][E], w2 [G*Himp*d][F]."""
+    e = torch.float32 if shape.dtype == TB_F32 else torch.bfloat16
+    N = shape.n_slots * shape.n_imp_heads * shape.d_imp
+    _expect("h", h, shape.tokens * shape.hidden, e)
+    _expect("w1", w1, shape.inner * shape.hidden, e)
+    _expect("w2", w2, N * shape.inner, e)
+    _expect("q_imp", q_imp, shape.n_slots * shape.tokens * shape.n_imp_heads * shape.d_imp, e)
+    _check("tb_predict_queries", lib().tb_predict_queries(
+        ctypes.byref(shape), _ptr(h), _ptr(w1), _ptr(w2), _ptr(q_imp), _ptr(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def step_args(shape, params, *, q, q_imp, k_new, v_new, refresh, w, k_cache, v_cache, kp_cache,

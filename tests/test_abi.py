@@ -29,7 +29,7 @@ def _exported_symbols():
 def test_library_exports_every_declared_function():
     declared = _declared_functions()
     assert {"tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn", "tb_dense_attn",
-            "tb_decode_step"} <= set(declared)
+            "tb_decode_step", "tb_predict_queries", "tb_mlp_workspace_bytes"} <= set(declared)
     exported = _exported_symbols()
     missing = [f for f in declared if f not in exported]
     assert not missing, missing
@@ -154,6 +154,29 @@ def test_dense_attn_argument_checks():
     bad = _shape(head_dim=96)
     assert L.tb_dense_attn(ctypes.byref(bad), fake, fake, fake, fake, scale, fake, fake, need,
                            None) == tbl.TB_EUNSUPPORTED
+
+
+def test_predict_queries_argument_checks():
+    L = tbl.lib()
+    mk = tbl.make_mlp_shape
+    good = mk(16, 4096, 1024, 4, 32, 32, tbl.TB_BF16, tbl.TB_ACT_SILU)
+    need = tbl.mlp_workspace_bytes(good)
+    assert need > 0
+    fake = ctypes.c_void_p(1 << 20)
+    call = lambda sh, h=fake, w1=fake, w2=fake, q=fake, ws=fake, nb=need: L.tb_predict_queries(  # noqa: E731
+        ctypes.byref(sh), h, w1, w2, q, ws, nb, None)
+    assert call(good, h=None) == tbl.TB_EINVAL
+    assert call(good, w2=ctypes.c_void_p((1 << 20) + 8)) == tbl.TB_EINVAL
+    assert call(good, nb=need - 1) == tbl.TB_EWORKSPACE
+    assert call(good, ws=ctypes.c_void_p((1 << 20) + 64)) == tbl.TB_EINVAL
+    assert call(mk(0, 4096, 1024, 4, 32, 32, tbl.TB_BF16)) == tbl.TB_EINVAL
+    assert call(mk(65, 4096, 1024, 4, 32, 32, tbl.TB_BF16)) == tbl.TB_EUNSUPPORTED
+    assert call(mk(16, 4000, 1024, 4, 32, 32, tbl.TB_BF16)) == tbl.TB_EUNSUPPORTED
+    assert call(mk(16, 4096, 1000, 4, 32, 32, tbl.TB_BF16)) == tbl.TB_EUNSUPPORTED
+    assert call(mk(16, 4096, 1024, 1, 3, 5, tbl.TB_BF16)) == tbl.TB_EUNSUPPORTED
+    assert call(mk(16, 4096, 1024, 4, 32, 32, tbl.TB_BF16, 7)) == tbl.TB_EUNSUPPORTED
+    assert call(mk(16, 4096, 1024, 4, 32, 32, 9)) == tbl.TB_EUNSUPPORTED
+    assert tbl.mlp_workspace_bytes(mk(65, 4096, 1024, 4, 32, 32, tbl.TB_BF16)) == 0
 
 
 def test_decode_step_argument_checks():
