@@ -15,6 +15,8 @@ Prints one JSON line.  Extra legs:
   dense_attention  the dense decode-attention kernel over the whole context at
                 the same shape (the baseline of the pages' speedup claims);
   predictor_mlp the importance-query producer MLP (weight-streaming bound);
+  offload       a 256K-context step with K/V in pinned host memory against
+                dense attention over the same offloaded caches;
   cpu_baseline  the fp64 C oracle's decode step on the host (1 thread), on a
                 bounded number of steps.
 """
@@ -35,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 from query_aware_kv_amd import synth  # noqa: E402
 from query_aware_kv_amd import tokenbutler as tbl  # noqa: E402
-from query_aware_kv_amd.workloads import LLAMA_32K  # noqa: E402
+from query_aware_kv_amd.workloads import LLAMA_32K, OFFLOAD_256K  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_llama3_8b_ctx32k_traffic.json")
@@ -84,6 +86,71 @@ def measured_traffic() -> float | None:
         return None
 
 
+def offload_leg(steps: int) -> dict:
+    """The 256K-context step with K and V in pinned host memory (read over
+    the host link) against dense attention over the same offloaded caches.
+    Host-link bytes: the unique gathered rows (sparse) or every row (dense)."""
+    w = OFFLOAD_256K
+    dev = "cuda:0"
+    log(f"bench: offload leg, generating {w.name}")
+    pre = synth.prefill(w)
+    inp = synth.step_inputs(w, 0, pre)
+    shape = tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
+                           w.d_imp, w.ctx_cap, synth.torch_dtype(w))
+    params = tbl.make_params(w.budget, w.radius, w.n_sink, w.n_local)
+    Kh, Vh = pre.K.pin_memory(), pre.V.pin_memory()
+    del pre
+    W = synth.draw_w(w).to(dev)
+    Kp = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=Kh.dtype, device=dev)
+    tbl.project_keys(shape, Kh, W, torch.zeros(w.batch, dtype=torch.int32, device=dev), w.ctx0,
+                     Kp)
+    ws = tbl.alloc_workspace(shape, params, dev)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
+    q, qi = inp.q.to(dev), inp.q_imp.to(dev)
+    kn, vn = inp.k_new.to(dev), inp.v_new.to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device=dev)
+    cnt = torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev)
+    bits = torch.zeros((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)), dtype=torch.int32,
+                       device=dev)
+    keep = torch.zeros(w.batch, dtype=torch.int32, device=dev)
+    args = tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=True, w=W,
+                         k_cache=Kh, v_cache=Vh, kp_cache=Kp, ctx_len=ctx,
+                         softmax_scale=w.softmax_scale, sel_idx=None, sel_count=cnt,
+                         sel_bits=bits, keep_from=keep, out=out)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, k):
+        fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / k
+
+    ms_step = timed(lambda: tbl.decode_step(shape, params, args, ws), steps)
+    ms_reuse = timed(lambda: tbl.sparse_attn(shape, q, Kh, Vh, None, 0, None, keep, ctx,
+                                             w.softmax_scale, out, ws, sel_bits=bits), steps)
+    ms_dense = timed(lambda: tbl.dense_attn(shape, q, Kh, Vh, ctx, w.softmax_scale, out, ws),
+                     max(2, steps // 4))
+    uniq, _ = unique_rows(bits, w, w.ctx)
+    row = w.head_dim * w.elt_bytes
+    sparse_bytes, dense_bytes = uniq * 2 * row, w.ctx * w.n_kv_heads * 2 * row
+    res = {"workload": w.name, "ctx": w.ctx, "budget": w.budget, "caches": "pinned host memory",
+           "step_ms": ms_step, "reuse_step_ms": ms_reuse, "dense_ms": ms_dense,
+           "speedup_vs_dense": ms_dense / ms_step,
+           "reuse_speedup_vs_dense": ms_dense / ms_reuse,
+           "step_host_link_GBs": sparse_bytes / (ms_step * 1e-3) / 1e9,
+           "dense_host_link_GBs": dense_bytes / (ms_dense * 1e-3) / 1e9,
+           "gathered_bytes": sparse_bytes, "dense_bytes": dense_bytes}
+    log(f"bench: offload 256K: step {ms_step:.2f} ms (reuse {ms_reuse:.2f} ms), dense "
+        f"{ms_dense:.2f} ms -> {ms_dense / ms_step:.2f}x; host link "
+        f"{res['step_host_link_GBs']:.1f} / {res['dense_host_link_GBs']:.1f} GB/s")
+    return res
+
+
 def cpu_baseline(w, pre, inp, seconds: float, max_steps: int) -> dict:
     import oracle as orc
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
@@ -118,6 +185,8 @@ def main() -> int:
                     help="tokens always kept at the start of the context (sink buffer)")
     ap.add_argument("--n-local", type=int, default=0,
                     help="most recent tokens always kept (local window)")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the 256K CPU-offloaded K/V leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
@@ -251,6 +320,8 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
 
+    offload = None if a.no_offload else offload_leg(max(4, min(a.steps, 20)))
+
     cpu = None
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle")
@@ -291,6 +362,7 @@ def main() -> int:
                                     "slots": 4, "imp_heads": w.n_imp_heads, "d_imp": w.d_imp},
                           "us_per_call": ms_mlp * 1e3, "algorithmic_bytes": mlp_bytes,
                           "achieved": mlp_gbs, "frac": mlp_gbs / PEAK_HBM_GBS},
+        "offload": offload,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -48,6 +48,13 @@
  *   rounded once (to nearest even) to the dtype; scores are fp32 fused
  *   multiply-add chains in ascending d_imp order starting from +0; attention
  *   accumulates in fp32.  Inputs must be finite.
+ * - Offloading ([ABS], [RES]: decoding with the cache in CPU memory): the K
+ *   and V caches may live in device memory or in pinned host memory that is
+ *   mapped for the device (hipHostMalloc; pass the device-side address from
+ *   hipHostGetDevicePointer).  The kernels then read only the rows they use
+ *   over the host link and write appended rows there; the projected-key
+ *   cache, queries, scores, selection state and workspace stay in device
+ *   memory.  Results do not depend on where the caches live.
  * - Alignment: tensors read or written in 16-byte pieces (K/V/Kp caches, q,
  *   W, k_new, v_new, the scores given to tb_select) must be 16-byte aligned,
  *   else TB_EINVAL.

@@ -114,12 +114,39 @@ def _ptr(t: torch.Tensor | None):
     return _vp(t.data_ptr())
 
 
-def _expect(name: str, t: torch.Tensor | None, numel: int, dtype=None) -> None:
-    """Host-side size check of a tensor against the shape it must have."""
+_hip = None
+
+
+def _cache_ptr(t: torch.Tensor | None):
+    """Pointer of a K or V cache for the kernels.  A cache may live in device
+    memory or, offloaded, in pinned host memory that the GPU reads over the
+    host link; for the latter the device-side address is taken from
+    hipHostGetDevicePointer, which also proves that the GPU can reach it."""
+    global _hip
+    if t is None or t.is_cuda:
+        return _ptr(t)
+    if not t.is_pinned():
+        raise ValueError("an offloaded cache must be pinned host memory (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtokenbutler must be contiguous")
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+    dev = _vp()
+    rc = _hip.hipHostGetDevicePointer(ctypes.byref(dev), _vp(t.data_ptr()), 0)
+    if rc != 0 or not dev.value:
+        raise RuntimeError(f"pinned cache is not mapped for the GPU (hip error {rc})")
+    return dev
+
+
+def _expect(name: str, t: torch.Tensor | None, numel: int, dtype=None,
+            host_ok: bool = False) -> None:
+    """Host-side size check of a tensor against the shape it must have
+    (host_ok: a pinned host tensor is accepted too, for offloaded caches)."""
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_cuda and not (host_ok and t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor"
+                         + (" or pinned host memory" if host_ok else ""))
     if t.numel() != numel:
         raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
     if dtype is not None and t.dtype != dtype:
@@ -176,12 +203,12 @@ def alloc_workspace(shape: Shape, params: SelectParams | None = None, device="cu
 
 def project_keys(shape, k_cache, w, pos0, n_tokens, kp_cache, stream=None):
     e = _elt(shape)
-    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
     _expect("kp_cache", kp_cache, _cache_numel(shape, shape.d_imp), e)
     _expect("w", w, shape.head_dim * shape.d_imp, e)
     _expect("pos0", pos0, shape.batch, torch.int32)
     _check("tb_project_keys", lib().tb_project_keys(
-        ctypes.byref(shape), _ptr(k_cache), _ptr(w), _ptr(pos0), int(n_tokens),
+        ctypes.byref(shape), _cache_ptr(k_cache), _ptr(w), _ptr(pos0), int(n_tokens),
         _ptr(kp_cache), _stream(stream)))
 
 
@@ -220,8 +247,8 @@ def sparse_attn(shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count, keep
     qn = shape.batch * shape.n_q_heads * shape.head_dim
     _expect("q", q, qn, e)
     _expect("out", out, qn, e)
-    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
-    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
+    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
     if sel_idx is not None:
         _expect("sel_idx", sel_idx, rows * int(sel_stride), torch.int32)
     _expect("sel_count", sel_count, rows, torch.int32)
@@ -229,7 +256,7 @@ def sparse_attn(shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count, keep
     _expect("keep_from", keep_from, shape.batch, torch.int32)
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _check("tb_sparse_attn", lib().tb_sparse_attn(
-        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx),
+        ctypes.byref(shape), _ptr(q), _cache_ptr(k_cache), _cache_ptr(v_cache), _ptr(sel_idx),
         int(sel_stride), _ptr(sel_count), _ptr(sel_bits), _ptr(keep_from), _ptr(ctx_len),
         float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
@@ -241,11 +268,11 @@ def dense_attn(shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, ws, stre
     qn = shape.batch * shape.n_q_heads * shape.head_dim
     _expect("q", q, qn, e)
     _expect("out", out, qn, e)
-    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
-    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
+    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _check("tb_dense_attn", lib().tb_dense_attn(
-        ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+        ctypes.byref(shape), _ptr(q), _cache_ptr(k_cache), _cache_ptr(v_cache), _ptr(ctx_len),
         float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
         _stream(stream)))
 
@@ -296,8 +323,8 @@ def step_args(shape, params, *, q, q_imp, k_new, v_new, refresh, w, k_cache, v_c
     _expect("k_new", k_new, shape.batch * shape.n_kv_heads * n_new * shape.head_dim, e)
     _expect("v_new", v_new, shape.batch * shape.n_kv_heads * n_new * shape.head_dim, e)
     _expect("w", w, shape.head_dim * shape.d_imp, e)
-    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e)
-    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e)
+    _expect("k_cache", k_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
+    _expect("v_cache", v_cache, _cache_numel(shape, shape.head_dim), e, host_ok=True)
     _expect("kp_cache", kp_cache, _cache_numel(shape, shape.d_imp), e)
     _expect("ctx_len", ctx_len, shape.batch, torch.int32)
     _expect("sel_idx", sel_idx, rows * selection_capacity(shape, params), torch.int32)
@@ -307,7 +334,8 @@ def step_args(shape, params, *, q, q_imp, k_new, v_new, refresh, w, k_cache, v_c
     a = StepArgs()
     a.q, a.q_imp, a.k_new, a.v_new = _ptr(q), _ptr(q_imp), _ptr(k_new), _ptr(v_new)
     a.n_new, a.refresh = n_new, int(bool(refresh))
-    a.w, a.k_cache, a.v_cache, a.kp_cache = _ptr(w), _ptr(k_cache), _ptr(v_cache), _ptr(kp_cache)
+    a.w, a.k_cache, a.v_cache = _ptr(w), _cache_ptr(k_cache), _cache_ptr(v_cache)
+    a.kp_cache = _ptr(kp_cache)
     a.ctx_len, a.softmax_scale = _ptr(ctx_len), float(softmax_scale)
     a.sel_idx, a.sel_count, a.sel_bits = _ptr(sel_idx), _ptr(sel_count), _ptr(sel_bits)
     a.keep_from, a.out = _ptr(keep_from), _ptr(out)

@@ -109,5 +109,13 @@ LONG_128K = Workload("long_ctx128k", batch=1, layers=1, n_q_heads=32, n_kv_heads
                      steps=1, budget=4096, radius=1, interval=1, plant_per_head=0,
                      plant_runs=16, plant_run_len=32, plant_shift=3.0, seed=5)
 
+# Offloading: 256K context with the K/V caches in pinned host memory (the
+# pages report the offloaded regime at 256K+ tokens), budget 10 %, no planting.
+OFFLOAD_256K = Workload("offload_ctx256k", batch=1, layers=1, n_q_heads=32, n_kv_heads=8,
+                        n_imp_heads=32, head_dim=128, d_imp=32, dtype="bf16", ctx0=262143,
+                        steps=1, budget=_budget(0.10, 262144), radius=0, interval=1,
+                        plant_per_head=0, plant_runs=0, plant_run_len=0, plant_shift=0.0,
+                        seed=6)
+
 ALL = [TINY_F32, LLAMA_32K, BATCHED_8K, INTERVAL_16K, LONG_128K]
 BY_NAME = {w.name: w for w in ALL}
