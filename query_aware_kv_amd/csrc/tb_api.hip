@@ -64,6 +64,8 @@ struct Ws {
     float *part_o;
     float *part_ml;
     uint32_t *counters;
+    uint16_t *keys16;
+    uint16_t *sample16;
 };
 
 Ws carve(void *ws, const WsLayout &L)
@@ -71,7 +73,8 @@ Ws carve(void *ws, const WsLayout &L)
     char *base = (char *)ws;
     return Ws{(float *)(base + L.scores),
               (float *)(base + L.part_o), (float *)(base + L.part_ml),
-              (uint32_t *)(base + L.counters)};
+              (uint32_t *)(base + L.counters), (uint16_t *)(base + L.keys16),
+              (uint16_t *)(base + L.sample16)};
 }
 
 int check_ws(const tb_shape &s, void *ws, size_t ws_bytes, WsLayout *L)
@@ -178,7 +181,7 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     return hip_rc(launch_score(*shape, q_imp, const_cast<void *>(kp_cache), ctx_len, scores, 0,
-                               nullptr, nullptr, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                (hipStream_t)stream));
 }
 
@@ -197,7 +200,7 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
                                 sel_capacity(*shape, *params), sel_count, topb_idx, sel_bits,
-                                nullptr, 0, (hipStream_t)stream));
+                                nullptr, 0, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
@@ -303,10 +306,10 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     if (a->refresh) {
         TB_TRY(hip_rc(launch_score(*shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
                                    fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
-                                   a->k_cache, a->v_cache, st)));
+                                   a->k_cache, a->v_cache, W.keys16, W.sample16, st)));
         TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
                                     a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
-                                    st)));
+                                    W.keys16, W.sample16, st)));
     }
     return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
                               a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,

@@ -77,6 +77,17 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return
 
 __device__ __forceinline__ int clamp_len(int v, int cap) { return v < 0 ? 0 : (v > cap ? cap : v); }
 
+// Order-preserving u32 key of an fp32 score: larger scores get larger keys,
+// -0.0 and +0.0 share one key, and every finite score's key is >= 2^23 (so
+// key 0 can mark "no score").
+__device__ __forceinline__ uint32_t score_key(float s)
+{
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u)
+        u = 0u; // -0.0 ties with +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ---------------------------------------------------------------- wave ops
 // Cross-lane steps through DPP row permutations (no LDS round trip); out of
 // row sources read 0.
@@ -142,6 +153,8 @@ struct WsLayout {
     size_t part_o;   // attention partial sums [b][Hq][nchunk][D] fp32
     size_t part_ml;  // attention partial (max, sum) [b][Hq][nchunk][2] fp32
     size_t counters; // attention arrival counters [b][Hkv] u32 (kept zero)
+    size_t keys16;   // top 16 bits of each score's key [b][Himp][cap] u16 (fused step)
+    size_t sample16; // the same for positions 8m, compact [b][Himp][sample16_stride] u16
     size_t total;
 };
 
@@ -149,6 +162,8 @@ inline int attn_chunks(int cap) { return (cap + kAttnChunk - 1) / kAttnChunk; }
 inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 
 inline int dense_chunks(int cap) { return (cap + kDenseChunk - 1) / kDenseChunk; }
+// u16 entries per row of the compact sample (positions 8m), a multiple of 8
+inline int sample16_stride(int cap) { return ((cap + 7) / 8 + 7) & ~7; }
 // Chunk partials are laid out per kernel's own chunk count; the region fits
 // the larger of the two.
 inline int max_chunks(int cap)
@@ -169,6 +184,11 @@ inline WsLayout ws_layout(const tb_shape &s)
     off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * 2 * sizeof(float));
     L.counters = off;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
+    L.keys16 = off;
+    off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(uint16_t));
+    L.sample16 = off;
+    off += align_up((size_t)s.batch * s.n_imp_heads * sample16_stride(s.ctx_cap) *
+                    sizeof(uint16_t));
     L.total = off;
     return L;
 }
@@ -184,16 +204,22 @@ hipError_t launch_append_project(const tb_shape &s, const void *k_new, const voi
 // appends the n_new rows of k_new / v_new at [ctx - n_new, ctx), projects
 // and scores them.
 int score_max_fused_new();
+// When keys16 is not NULL the launch also stores the top 16 bits of every
+// score's key into keys16[row][t] and, for positions t = 8m, into
+// sample16[row][m] (row stride sample16_stride(cap)).
 hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
                         const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
                         const void *v_new, const void *w, void *k_cache, void *v_cache,
-                        hipStream_t st);
+                        uint16_t *keys16, uint16_t *sample16, hipStream_t st);
 // Selection; when keep_from is not NULL it also records
-// keep_from[b] = max(0, ctx_len[b] - n_new).
+// keep_from[b] = max(0, ctx_len[b] - n_new).  keys16 / sample16 (or NULL):
+// the score launch's 16-bit keys of the same scores, which let the first
+// pass read half the bytes.
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
-                         int32_t *keep_from, int n_new, hipStream_t st);
+                         int32_t *keep_from, int n_new, const uint16_t *keys16,
+                         const uint16_t *sample16, hipStream_t st);
 hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *sel_idx, int sel_stride,
                        const int32_t *sel_count, const uint32_t *sel_bits,

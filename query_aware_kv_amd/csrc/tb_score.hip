@@ -15,7 +15,9 @@
 //
 // Precision contract: a score is the fp32 fused multiply-add chain over the
 // d coordinates in ascending order, starting from +0; this fp32 value is the
-// selection key.
+// selection key.  In the fused step the top 16 bits of its order-preserving
+// key are stored as well (and compactly for positions 8m), so the selection
+// can classify positions from half the bytes.
 //
 // When the call also appends tokens, one extra work-group per (sequence, KV
 // head) -- the first one dispatched -- writes the new K/V rows into the
@@ -42,14 +44,29 @@ struct ScoreArgs {
     const void *k_new, *v_new; // [b][Hkv][n_new][D]
     const void *w;             // [D][d]
     void *k_cache, *v_cache;
+    uint16_t *keys16;   // [b][Himp][cap] top 16 key bits of every score, or NULL
+    uint16_t *sample16; // [b][Himp][s16] the same for positions 8m
+    int s16;
 };
+
+// Stores the score of (row, t) and, when asked, its 16-bit key.
+__device__ __forceinline__ void put_score(const ScoreArgs &a, size_t row, int t, float v)
+{
+    a.scores[row * a.cap + t] = v;
+    if (a.keys16 != nullptr) {
+        const uint16_t k16 = (uint16_t)(score_key(v) >> 16);
+        a.keys16[row * a.cap + t] = k16;
+        if ((t & 7) == 0)
+            a.sample16[row * a.s16 + (t >> 3)] = k16;
+    }
+}
 
 template <typename T, int DI, int GI>
 __device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, int t,
                                             const float (&k)[DI], bool valid)
 {
-    const T *qb = (const T *)a.q_imp + ((size_t)b * a.Himp + (size_t)g * GI) * DI;
-    float *sb = a.scores + ((size_t)b * a.Himp + (size_t)g * GI) * a.cap;
+    const size_t row0 = (size_t)b * a.Himp + (size_t)g * GI;
+    const T *qb = (const T *)a.q_imp + row0 * DI;
 #pragma unroll
     for (int hh = 0; hh < GI; ++hh) {
         float acc = 0.f;
@@ -57,7 +74,7 @@ __device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, in
         for (int j = 0; j < DI; ++j)
             acc = fmaf(to_f32(qb[hh * DI + j]), k[j], acc);
         if (valid)
-            sb[(size_t)hh * a.cap + t] = acc;
+            put_score(a, row0 + hh, t, acc);
     }
 }
 
@@ -145,7 +162,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
 #pragma unroll
             for (int j = 0; j < DI; ++j)
                 acc = fmaf(to_f32(qh[j]), sKp[r][j], acc);
-            a.scores[((size_t)b * a.Himp + (size_t)g * GI + hh) * a.cap + t_new + r] = acc;
+            put_score(a, (size_t)b * a.Himp + (size_t)g * GI + hh, t_new + r, acc);
         }
         return;
     }
@@ -212,7 +229,7 @@ int score_max_fused_new() { return kMaxFusedNew; }
 hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
                         const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
                         const void *v_new, const void *w, void *k_cache, void *v_cache,
-                        hipStream_t st)
+                        uint16_t *keys16, uint16_t *sample16, hipStream_t st)
 {
     ScoreArgs a;
     a.q_imp = q_imp;
@@ -230,6 +247,9 @@ hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
     a.w = w;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
+    a.keys16 = keys16;
+    a.sample16 = sample16;
+    a.s16 = sample16_stride(s.ctx_cap);
     if (s.dtype == TB_BF16)
         return score_dtype<bf16_t>(s, a, st);
     return score_dtype<float>(s, a, st);

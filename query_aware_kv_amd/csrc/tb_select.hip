@@ -57,14 +57,6 @@ static_assert(kSampleBins <= kCopies * kCopyStride, "sample histogram reuses the
 // misc words
 constexpr int kMiscScan = 8;   // kSelWaves + 1 words of block-scan scratch
 
-__device__ __forceinline__ uint32_t score_key(float s)
-{
-    uint32_t u = __float_as_uint(s);
-    if (u == 0x80000000u)
-        u = 0u; // -0.0 ties with +0.0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Exclusive scan of popcount(words[w]) over w < nw into out[w] (skipped when
 // out is NULL); returns the total to every thread.  wsum: kSelWaves words of
 // LDS scratch.
@@ -241,14 +233,16 @@ __device__ __forceinline__ uint32_t mask_below(int w, int x)
     return c <= 0 ? 0u : (c >= 32 ? 0xFFFFFFFFu : (1u << c) - 1u);
 }
 
-template <int WPT>
+template <int WPT, bool K16>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
     int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
     uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new,
-    int n_sink, int n_local)
+    int n_sink, int n_local, const uint16_t *__restrict__ keys16,
+    const uint16_t *__restrict__ sample16, int s16)
 {
+    static_assert(!K16 || WPT == 1, "16-bit first pass: one word per thread");
     extern __shared__ __align__(16) uint32_t lds[];
     uint32_t *hist = lds;                         // [kCopies][kCopyStride]
     uint32_t *tot = hist + kCopies * kCopyStride; // [256]
@@ -265,6 +259,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int b = blockIdx.y, i = blockIdx.x;
     const size_t rowid = (size_t)b * Himp + i;
     const float *row = scores + rowid * cap;
+    // With 16-bit keys, this thread's four sample keys (positions 8m,
+    // m = 4 tid .. 4 tid + 3) and its word's 32 keys are requested before
+    // the context length is known, the sample first so that its histogram
+    // can be built while the keys arrive (masked by position afterwards).
+    uint2 s16v = make_uint2(0u, 0u);
+    uint4 k16v[4] = {};
+    const bool k16vec = K16 && (cap & 7) == 0 && 32 * tid + 32 <= cap;
+    if constexpr (K16) {
+        if (4 * tid < s16)
+            s16v = *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + 4 * tid);
+        if (k16vec) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(keys16 + rowid * cap + 32 * tid);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                k16v[q] = src[q];
+        }
+    }
     const int n = clamp_len(ctx_len[b], cap);
     if (keep_from != nullptr && i == 0 && tid == 0)
         keep_from[b] = n - n_new > 0 ? n - n_new : 0;
@@ -286,13 +297,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     if (tid < 64)
         misc[tid] = 0u;
 
+    // full keys live in registers with one word per thread (not needed when
+    // the first pass reads the 16-bit keys)
+    constexpr bool REG = WPT > 0 && !K16;
     uint32_t keys[32];
-    if constexpr (WPT > 0)
+    if constexpr (REG)
         load_word_keys(row, tid, lo, hi, n, vec, keys);
     // fn(w, k) over this thread's words, k[e] the key of position 32w + e
     auto for_words = [&](auto &&fn) {
-        if constexpr (WPT > 0) {
+        if constexpr (REG) {
             fn(tid, keys);
+        } else if constexpr (WPT > 0) {
+            uint32_t k[32];
+            load_word_keys(row, tid, lo, hi, n, vec, k);
+            fn(tid, k);
         } else {
             for (int j = 0; j < nwt; ++j) {
                 uint32_t k[32];
@@ -360,7 +378,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             // ---- bracket tau from the keys at positions 8m ----
             // (keys 0, 8, 16, 24 of every word), binned by their top 12 bits
             auto sample_word = [&](int j, uint32_t (&s4)[4]) {
-                if constexpr (WPT > 0) {
+                if constexpr (K16) {
+                    // the 16-bit keys of positions 8(4 tid + q), as the top
+                    // half of a key (enough for the 12-bit sample bins)
+                    (void)j;
+                    const uint32_t pair[2] = {s16v.x, s16v.y};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int p = 8 * (4 * tid + q);
+                        const uint32_t k16 = (pair[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+                        s4[q] = p < n && p >= lo && p < hi ? k16 << 16 : 0u;
+                    }
+                } else if constexpr (REG) {
                     (void)j;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
@@ -422,13 +451,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             // candidate words; then the candidates (key, position), per wave ----
             uint2 *cwave = cpair + wave * kWaveCap;
             uint32_t run = 0u, na = 0u;
-            for_words([&](int w, const auto &k) {
-                uint32_t wt = 0u, wc = 0u;
-#pragma unroll
-                for (int e = 0; e < 32; ++e) {
-                    wt |= (uint32_t)(k[e] > phim1) << e;
-                    wc |= (uint32_t)(k[e] - plo <= span) << e;
-                }
+            auto pass_word = [&](int w, uint32_t wt, uint32_t wc) {
                 if (w < nw) {
                     Tb[w] = wt;
                     Sb[w] = 0u;
@@ -466,7 +489,49 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                         }
                     }
                 }
-            });
+            };
+            if constexpr (K16) {
+                // this thread's word from the 16-bit keys: bin = key16 >> 4
+                uint32_t kw[16];
+                if (k16vec) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        kw[4 * q + 0] = k16v[q].x;
+                        kw[4 * q + 1] = k16v[q].y;
+                        kw[4 * q + 2] = k16v[q].z;
+                        kw[4 * q + 3] = k16v[q].w;
+                    }
+                } else {
+                    const uint16_t *src = keys16 + rowid * cap + 32 * tid;
+#pragma unroll
+                    for (int e2 = 0; e2 < 16; ++e2) {
+                        const int p = 32 * tid + 2 * e2;
+                        const uint32_t a0 = p < n ? src[2 * e2] : 0u;
+                        const uint32_t a1 = p + 1 < n ? src[2 * e2 + 1] : 0u;
+                        kw[e2] = a0 | (a1 << 16);
+                    }
+                }
+                uint32_t wt = 0u, wc = 0u;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int p = 32 * tid + e;
+                    const uint32_t bin = ((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 4;
+                    const bool valid = p < n && p >= lo && p < hi;
+                    wt |= (uint32_t)(valid && bin > b_hi) << e;
+                    wc |= (uint32_t)(valid && bin >= b_lo && bin <= b_hi) << e;
+                }
+                pass_word(tid, wt, wc);
+            } else {
+                for_words([&](int w, const auto &k) {
+                    uint32_t wt = 0u, wc = 0u;
+#pragma unroll
+                    for (int e = 0; e < 32; ++e) {
+                        wt |= (uint32_t)(k[e] > phim1) << e;
+                        wc |= (uint32_t)(k[e] - plo <= span) << e;
+                    }
+                    pass_word(w, wt, wc);
+                });
+            }
             na = wave_reduce(na, [](uint32_t x, uint32_t y) { return x + y; });
             if (lane == 0) {
                 tot[wave] = run;
@@ -676,11 +741,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         sel_count[rowid] = (int32_t)total;
 }
 
-template <int WPT>
+template <int WPT, bool K16>
 hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                     int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
-                    int32_t *keep_from, int n_new, hipStream_t st)
+                    int32_t *keep_from, int n_new, const uint16_t *keys16,
+                    const uint16_t *sample16, hipStream_t st)
 {
     // words per bitmap array, even so that the candidate pairs stay 8-byte aligned
     const int nwc = ((s.ctx_cap + 31) / 32 + 2) & ~1;
@@ -690,16 +756,17 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
     const size_t lds = ((size_t)kCopies * kCopyStride + 256 + 64 + 2 * (size_t)nwc + u) *
                        sizeof(uint32_t);
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<WPT>,
+        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<WPT, K16>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
             return e;
     }
     dim3 grid(s.n_imp_heads, s.batch);
-    hipLaunchKernelGGL(select_kernel<WPT>, grid, dim3(kSelThreads), lds, st, scores, ctx_len,
-                       s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx, sel_stride,
-                       sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap), keep_from,
-                       n_new, p.n_sink, p.n_local);
+    hipLaunchKernelGGL((select_kernel<WPT, K16>), grid, dim3(kSelThreads), lds, st, scores,
+                       ctx_len, s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx,
+                       sel_stride, sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap),
+                       keep_from, n_new, p.n_sink, p.n_local, keys16, sample16,
+                       sample16_stride(s.ctx_cap));
     return hipGetLastError();
 }
 
@@ -708,12 +775,18 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
-                         int32_t *keep_from, int n_new, hipStream_t st)
+                         int32_t *keep_from, int n_new, const uint16_t *keys16,
+                         const uint16_t *sample16, hipStream_t st)
 {
 #define TB_SEL_ARGS                                                                          \
-    s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from, n_new, st
-    if ((s.ctx_cap + 31) / 32 <= kSelThreads) return select_t<1>(TB_SEL_ARGS);
-    return select_t<0>(TB_SEL_ARGS);
+    s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from,       \
+        n_new, keys16, sample16, st
+    if ((s.ctx_cap + 31) / 32 <= kSelThreads) {
+        if (keys16 != nullptr && sample16 != nullptr)
+            return select_t<1, true>(TB_SEL_ARGS);
+        return select_t<1, false>(TB_SEL_ARGS);
+    }
+    return select_t<0, false>(TB_SEL_ARGS);
 #undef TB_SEL_ARGS
 }
 
