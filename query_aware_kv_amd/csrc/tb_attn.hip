@@ -7,17 +7,19 @@
 // Grid: (position chunk of kAttnChunk tokens, KV head, sequence).  A
 // work-group handles one KV head and one chunk for all the query heads that
 // share it (GQA):
-//   1. Each query head's membership in the chunk comes either from its
-//      selection bitmap (one 32-bit word per 32 positions, read directly) or
-//      from its ascending selection list (the chunk's segment is located by a
-//      wave-parallel search, 64 samples per round); the always-kept range
+//   1. Each query head is served by 8/GQ of the eight waves, each wave taking
+//      a part of the chunk.  A wave's membership words come, one per lane,
+//      either straight from the head's selection bitmap (one 32-bit word per
+//      32 positions) or from its ascending selection list (the chunk's
+//      segment is located by a wave-parallel search, 64 samples per round,
+//      and scattered into an LDS bitmap); the always-kept range
 //      [keep_from, n) is added to every head.
-//   2. Each query head is served by 8/GQ of the eight waves, each wave taking
-//      a part of the chunk and compacting that head's positions in it with
-//      ballots; the head's waves then split the concatenated list evenly.
-//      Rows that several query heads of the group select are requested by
-//      sibling waves of the same work-group at about the same time, so the
-//      repeats are served from cache and HBM sees each row about once.
+//   2. Two consecutive words are the 64-bit mask of 64 positions, so the
+//      wave compacts its positions from scalar masks with no ballot and no
+//      work-group barrier.  Rows that several query heads of the group
+//      select are requested by sibling waves of the same work-group at about
+//      the same time, so the repeats are served from cache and HBM sees each
+//      row about once.
 //   3. Rows stream through the lanes in 16-byte pieces (D*elt/16 lanes per
 //      row, several rows per wave, four rows in flight per row slot); each row
 //      slot keeps an online softmax (running max, sum, fp32 accumulator) for
@@ -92,7 +94,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 
     __shared__ uint32_t bm[GQ][NWD];
     __shared__ uint16_t hlist[kAttnWaves][PW]; // positions of each wave's part
-    __shared__ uint32_t wcnt[kAttnWaves];
     __shared__ float mrg_m[GQ][NS];
     __shared__ float mrg_l[GQ][NS];
     __shared__ float mrg_f[GQ][NS];
@@ -109,23 +110,23 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int c0 = c * kAttnChunk;
     const size_t head0 = (size_t)b * a.Hq + (size_t)g * GQ; // first query head of the group
     const int slot = lane / LPR, sub = lane % LPR;
-    static_assert(GQ * NWD <= kAttnThreads, "one bitmap word per thread");
 
-    // Wave w serves query head hw = w / WPH on part w % WPH of the chunk.
+    // Wave w serves query head hw = w / WPH on part wpart = w % WPH of the
+    // chunk: positions [c0 + wpart * PW, c0 + (wpart + 1) * PW), which are
+    // bitmap words wpart * WPW .. + WPW - 1 of the chunk, one per lane.
     const int hw = wave / WPH, wpart = wave % WPH;
+    constexpr int WPW = PW / 32;
+    static_assert(WPW <= 64 && WPW % 2 == 0, "a part's words fit one wave, in pairs");
     // Everything that does not depend on the lengths is requested first: the
     // q slice of this lane for the wave's head (kept in the storage type;
-    // bf16 pairs feed v_dot2) and, in bitmap mode, this thread's membership
-    // word.
+    // bf16 pairs feed v_dot2) and, in bitmap mode, this lane's word.
     const uint4 qh = *reinterpret_cast<const uint4 *>(q + (head0 + hw) * D + sub * EPL);
-    uint32_t word0 = 0u;
+    const int p0w = c0 + 32 * (wpart * WPW + lane); // first position of this lane's word
+    uint32_t word = 0u;
     if constexpr (BITMAP) {
-        if (tid < GQ * NWD) {
-            const int hl = tid / NWD, w = tid % NWD;
-            const int i = (int)((long)(g * GQ + hl) * a.Himp / a.Hq);
-            const int p0 = c0 + 32 * w; // first position of this word
-            if (p0 < a.cap)
-                word0 = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride + (p0 >> 5)];
+        if (lane < WPW && p0w < a.cap) {
+            const int i = (int)((long)(g * GQ + hw) * a.Himp / a.Hq);
+            word = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride + (p0w >> 5)];
         }
     }
     const int kf_raw = a.keep_from != nullptr ? a.keep_from[b] : a.cap;
@@ -134,24 +135,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const bool active = c0 < n;
 
     if (active) {
-        // ---- 1. per-head membership of this chunk ----
+        // ---- 1. the wave's membership words ----
         const int kf = clamp_len(kf_raw, n);
-        if constexpr (BITMAP) {
-            if (tid < GQ * NWD) {
-                const int hl = tid / NWD, w = tid % NWD;
-                const int p0 = c0 + 32 * w;
-                uint32_t word = p0 < c1 ? word0 : 0u;
-                // clip to [c0, c1) and add the always-kept range
-                const int lo = max(kf, p0), hi = min(c1, p0 + 32);
-                if (hi - p0 < 32)
-                    word &= hi <= p0 ? 0u : ((1u << (hi - p0)) - 1u);
-                if (lo < hi) {
-                    const uint32_t upto = hi - p0 == 32 ? 0xffffffffu : ((1u << (hi - p0)) - 1u);
-                    word |= upto & ~((1u << (lo - p0)) - 1u);
-                }
-                bm[hl][w] = word;
-            }
-        } else {
+        if constexpr (!BITMAP) {
+            // list mode: the group's lists are scattered into an LDS bitmap first
             for (int e = tid; e < GQ * NWD; e += kAttnThreads)
                 (&bm[0][0])[e] = 0u;
             __syncthreads();
@@ -170,55 +157,40 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                         atomicOr(&bm[hl][(t - c0) >> 5], 1u << ((t - c0) & 31));
                 }
             }
-            for (int t = max(kf, c0) + tid; t < c1; t += kAttnThreads)
-#pragma unroll
-                for (int hl = 0; hl < GQ; ++hl)
-                    atomicOr(&bm[hl][(t - c0) >> 5], 1u << ((t - c0) & 31));
+            __syncthreads();
+            if (lane < WPW)
+                word = bm[hw][wpart * WPW + lane];
         }
-        __syncthreads();
-
-        // ---- 2. this wave's positions, compacted by ballots ----
-        {
-            uint32_t run = 0u;
-#pragma unroll
-            for (int k = 0; k < PW / 64; ++k) {
-                const int pos = wpart * PW + 64 * k + lane;
-                const bool in = (bm[hw][pos >> 5] >> (pos & 31)) & 1u;
-                const unsigned long long m = __ballot(in);
-                if (in)
-                    hlist[wave][run + __builtin_amdgcn_mbcnt_hi(
-                                          (uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-                        (uint16_t)pos;
-                run += __popcll(m);
+        if (lane < WPW) {
+            // clip to [c0, c1) and add the always-kept range [kf, n)
+            const int lo = max(kf, p0w), hi = min(c1, p0w + 32);
+            if (hi - p0w < 32)
+                word &= hi <= p0w ? 0u : ((1u << (hi - p0w)) - 1u);
+            if (lo < hi) {
+                const uint32_t upto = hi - p0w == 32 ? 0xffffffffu : ((1u << (hi - p0w)) - 1u);
+                word |= upto & ~((1u << (lo - p0w)) - 1u);
             }
-            if (lane == 0)
-                wcnt[wave] = run;
         }
-        __syncthreads();
 
-        // ---- 3. stream the head's rows ----
-        // The head's positions are the concatenation of its WPH parts; each
-        // of its waves takes an equal share, and each row slot of a wave an
-        // interleaved share of that.
-        uint32_t pre[WPH], nh = 0u;
+        // ---- 2. the wave's positions, in order ----
+        // Two consecutive words are the 64-bit membership mask of 64
+        // positions; a lane's slot is the count of set bits below it.
+        uint32_t nh = 0u;
 #pragma unroll
-        for (int pp = 0; pp < WPH; ++pp) {
-            pre[pp] = nh;
-            nh += wcnt[hw * WPH + pp];
+        for (int k = 0; k < WPW / 2; ++k) {
+            const uint32_t m_lo = __builtin_amdgcn_readlane(word, 2 * k);
+            const uint32_t m_hi = __builtin_amdgcn_readlane(word, 2 * k + 1);
+            const uint64_t msk = (uint64_t)m_lo | ((uint64_t)m_hi << 32);
+            if ((msk >> lane) & 1ull)
+                hlist[wave][nh + __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u))] =
+                    (uint16_t)(wpart * PW + 64 * k + lane);
+            nh += (uint32_t)__popcll(msk);
         }
-        const uint32_t e0 = nh * wpart / WPH, e1 = nh * (wpart + 1) / WPH;
-        auto position = [&](uint32_t u) -> uint32_t { // u < nh
-            int src = hw * WPH;
-            uint32_t off = u;
-#pragma unroll
-            for (int pp = 1; pp < WPH; ++pp) {
-                const bool at = u >= pre[pp];
-                src = at ? hw * WPH + pp : src;
-                off = at ? u - pre[pp] : off;
-            }
-            return hlist[src][off];
-        };
+        // the list is written and read by this wave only
+        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- 3. stream the wave's rows ----
         float m = -INFINITY, l = 0.f, acc[EPL];
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
@@ -231,15 +203,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         // is used.  The loads are unconditional -- a missing row reads the
         // chunk's first row, which always exists, and is given weight 0 -- so
         // they issue back to back.
-        for (uint32_t base = e0 + slot; base < e1; base += kRowsInFlight * RPW) {
+        for (uint32_t base = slot; base < nh; base += kRowsInFlight * RPW) {
             uint32_t pos[kRowsInFlight];
             bool ok[kRowsInFlight];
             uint4 kk[kRowsInFlight], vv[kRowsInFlight];
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
                 const uint32_t u = base + r * RPW;
-                ok[r] = u < e1;
-                pos[r] = ok[r] ? position(u) : 0u;
+                ok[r] = u < nh;
+                pos[r] = ok[r] ? hlist[wave][u] : 0u;
             }
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
