@@ -26,7 +26,8 @@
 //      its wave's head in base 2, rescaling only when the running max grows.
 //      Lane dot products use v_dot2 on bf16 pairs and are reduced across the
 //      row's lanes with DPP row permutations.
-//   4. The row slots of a head are merged through LDS into one partial
+//   4. The row slots of a wave are merged in registers (DPP and the
+//      permlane swaps), the waves of a head through LDS, into one partial
 //      (max, sum, acc[D]) per query head and chunk.
 //   5. The last work-group of a (sequence, KV head) to arrive (device-scope
 //      counter) merges the chunk partials -- max and weights first, then the
@@ -89,16 +90,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     static_assert(GQ <= kAttnWaves && kAttnWaves % GQ == 0, "whole waves per query head");
     constexpr int WPH = kAttnWaves / GQ;     // waves per query head
     constexpr int PW = kAttnChunk / WPH;     // positions of one wave's part of the chunk
-    constexpr int NS = WPH * RPW;            // row slots per query head
-    static_assert(PW % 64 == 0 && NS <= 64, "parts of whole ballots; one lane per slot");
+    static_assert(PW % 64 == 0, "parts of whole 64-position masks");
 
     __shared__ uint32_t bm[GQ][NWD];
     __shared__ uint16_t hlist[kAttnWaves][PW]; // positions of each wave's part
-    __shared__ float mrg_m[GQ][NS];
-    __shared__ float mrg_l[GQ][NS];
-    __shared__ float mrg_f[GQ][NS];
-    __shared__ float mrg_acc[GQ][NS][D];
-    __shared__ float mrg_M[GQ], mrg_L[GQ];
+    __shared__ float mrg_m[GQ][WPH];
+    __shared__ float mrg_l[GQ][WPH];
+    __shared__ float mrg_acc[GQ][WPH][D];
     __shared__ CombineLds<GQ, kAttnThreads> cmb;
 
     const T *__restrict__ q = (const T *)a.q;
@@ -243,42 +241,45 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         }
 
         // ---- 4. merge each head's row slots into the chunk partial ----
-        // Every slot's (max, sum, acc) goes to LDS; one wave per head finds
-        // the head's max and each slot's weight, then one thread per (head,
-        // dim) sums the weighted accumulators.
+        // A wave's row slots merge in registers (DPP and the permlane
+        // swaps); the head's waves then meet in LDS, one thread per (head,
+        // dim) weighting each wave's accumulator by its max.
         {
-            const int ms = wpart * RPW + slot;
+            auto fmax2 = [](float x, float y) { return fmaxf(x, y); };
+            auto add2 = [](float x, float y) { return x + y; };
+            const float M = across_slots<LPR>(m, fmax2);
+            const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+            const float L = across_slots<LPR>(l * f, add2);
 #pragma unroll
             for (int e = 0; e < EPL; ++e)
-                mrg_acc[hw][ms][sub * EPL + e] = acc[e];
-            if (sub == 0) {
-                mrg_m[hw][ms] = m;
-                mrg_l[hw][ms] = l;
-            }
-        }
-        __syncthreads();
-        for (int h2 = wave; h2 < GQ; h2 += kAttnWaves) {
-            const float mv = lane < NS ? mrg_m[h2][lane] : -INFINITY;
-            const float M = wave_max(mv);
-            const float f = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-            const float Ls = wave_sum(lane < NS ? mrg_l[h2][lane] * f : 0.f);
-            if (lane < NS)
-                mrg_f[h2][lane] = f;
-            if (lane == 0) {
-                mrg_M[h2] = M;
-                mrg_L[h2] = Ls;
+                acc[e] = across_slots<LPR>(acc[e] * f, add2);
+            if (slot == 0) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e)
+                    mrg_acc[hw][wpart][sub * EPL + e] = acc[e];
+                if (sub == 0) {
+                    mrg_m[hw][wpart] = M;
+                    mrg_l[hw][wpart] = L;
+                }
             }
         }
         __syncthreads();
         static_assert((GQ * D) % 64 == 0, "whole waves in the partial loop (lane pairs)");
         for (int pi = tid; pi < GQ * D; pi += kAttnThreads) {
             const int h2 = pi / D, dim = pi % D;
-            float O = 0.f;
+            float M = -INFINITY;
 #pragma unroll
-            for (int s2 = 0; s2 < NS; ++s2)
-                O = fmaf(mrg_acc[h2][s2][dim], mrg_f[h2][s2], O);
-            publish_partial<D>(a.part_o, a.part_ml, (head0 + h2) * nchunk + c, dim, O,
-                               mrg_M[h2], mrg_L[h2]);
+            for (int pp = 0; pp < WPH; ++pp)
+                M = fmaxf(M, mrg_m[h2][pp]);
+            float O = 0.f, Ls = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < WPH; ++pp) {
+                const float mp = mrg_m[h2][pp];
+                const float f = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+                O = fmaf(mrg_acc[h2][pp][dim], f, O);
+                Ls = fmaf(mrg_l[h2][pp], f, Ls);
+            }
+            publish_partial<D>(a.part_o, a.part_ml, (head0 + h2) * nchunk + c, dim, O, M, Ls);
         }
     }
 
