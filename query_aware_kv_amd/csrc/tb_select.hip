@@ -10,23 +10,28 @@
 //   1. Scores become order-preserving u32 keys (-0 folded onto +0; positions
 //      >= n get key 0, below every real key).  Rows of up to 1024 words keep
 //      their keys in registers (read once, in 16-byte loads); longer rows
-//      re-read them (from L2) at each pass.
+//      re-read them (from L2) at each pass.  In the fused step the score
+//      launch has also stored the top 16 bits of every key (and compactly for
+//      positions 8m); rows of up to 1024 words then take steps 2's sample and
+//      first pass from those (half the bytes, the sample first), and read full
+//      keys only for the candidates and the fallback.
 //   2. The B-th largest key tau is bracketed from a sample of one position in
-//      eight (positions 8m): the sample goes into a 4096-bin histogram over
-//      its own key range, and two bins a safe margin either side of the
-//      sample quantile B/n bound a candidate key range.  One compare-only
-//      pass counts (by wave ballots) the keys above it and in it; when tau
-//      provably lies in the range and the candidates fit in LDS they are
-//      compacted there and the radix select below runs over them alone.
-//      Otherwise it runs over every key.
-//      Radix select: from the top, 8 bits per pass, over the keys that match
-//      the prefix found so far.  Over every key the histogram lives in LDS as
-//      16 copies (lane mod 16), padded so that equal digits in different
-//      copies fall in different banks; over the candidates one copy is
-//      enough.  A wave-wide suffix sum picks the digit holding the wanted
-//      key.  When every key of that digit is needed the search stops early.
-//      Result: the threshold tau and how many keys equal to it are kept (the
-//      lowest positions first).  Either route gives the same tau.
+//      eight (positions 8m): the sample goes into a 4096-bin histogram of the
+//      keys' top 12 bits, and two bins a safe margin either side of the
+//      sample quantile B/m (m: positions competing) bound a candidate range.
+//      One compare-only pass marks the keys above it (kept) and in it; the
+//      candidates' (key, position) pairs are compacted per wave into LDS and
+//      counted by their top 20 bits.  When tau provably lies in the range and
+//      the candidates fit, tau is found from that histogram and one over the
+//      low 12 bits of the candidates sharing its top 20 bits.  Otherwise a
+//      radix select runs over every key: from the top, 8 bits per pass, over
+//      the keys that match the prefix found so far, with the histogram in
+//      LDS as 16 copies (lane mod 16) padded so that equal digits in
+//      different copies fall in different banks; a wave-wide suffix sum picks
+//      the digit holding the wanted key, and the search stops early when
+//      every key of that digit is needed.  Result: the threshold tau and how
+//      many keys equal to it are kept (the lowest positions first).  Either
+//      route gives the same tau.
 //   3. Every thread builds its own words of the kept set T from its keys; a
 //      block scan of per-word tie counts settles ties at tau by position.
 //   4. Dilation by r is word-wise shifts of the bitmap, clipped to [0, n).

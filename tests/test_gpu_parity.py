@@ -136,6 +136,27 @@ def test_fused_step_full_size(w):
         np.testing.assert_array_equal(f64(dc.Kp[b][:, rows]), st.Kp[:, rows])
 
 
+@pytest.mark.parametrize("kw", [dict(ctx0=1996), dict(ctx0=1996, dtype="f32", head_dim=64, d_imp=16,
+                                                  n_sink=3, n_local=10)],
+                         ids=["bf16", "f32_sink_local"])
+def test_fused_step_odd_capacity(kw):
+    # a capacity that is not a multiple of 8 (1997): the selection's 16-bit
+    # keys are read one at a time instead of in 16-byte pieces
+    w = _small(**kw)
+    assert w.ctx_cap % 8 != 0
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in range(w.batch):
+        st = oracle_state(w, dc.pre, b)
+        ref = oracle_step(w, st, dc.pre, inp, 0, b)
+        got = lists_of(dc.sel, dc.cnt, b)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        assert float(np.abs(f64(out[b]) - ref).max()) <= TOL[w.dtype]
+
+
 def test_planted_tokens_are_found():
     # sanity of the synthetic workload, not a parity bar: with a shift of 4
     # score standard deviations nearly every planted token is selected
