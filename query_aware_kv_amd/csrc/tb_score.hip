@@ -61,21 +61,46 @@ __device__ __forceinline__ void put_score(const ScoreArgs &a, size_t row, int t,
     }
 }
 
+// The group's importance queries, requested in 16-byte pieces before any
+// score is stored (the stores could alias them for all the compiler knows,
+// which would otherwise serialise one load round trip per piece).
+template <typename T, int DI, int GI>
+__device__ __forceinline__ void load_queries(const ScoreArgs &a, int b, int g,
+                                             uint4 (&qv)[GI][DI * sizeof(T) / 16])
+{
+    const uint4 *qb = reinterpret_cast<const uint4 *>(
+        (const T *)a.q_imp + ((size_t)b * a.Himp + (size_t)g * GI) * DI);
+#pragma unroll
+    for (int hh = 0; hh < GI; ++hh)
+#pragma unroll
+        for (int p = 0; p < DI * (int)sizeof(T) / 16; ++p)
+            qv[hh][p] = qb[hh * (DI * sizeof(T) / 16) + p];
+}
+
 template <typename T, int DI, int GI>
 __device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, int t,
-                                            const float (&k)[DI], bool valid)
+                                            const float (&k)[DI], bool valid,
+                                            const uint4 (&qv)[GI][DI * sizeof(T) / 16])
 {
+    constexpr int EPC = 16 / sizeof(T);
     const size_t row0 = (size_t)b * a.Himp + (size_t)g * GI;
-    const T *qb = (const T *)a.q_imp + row0 * DI;
+    float acc[GI];
 #pragma unroll
     for (int hh = 0; hh < GI; ++hh) {
-        float acc = 0.f;
+        acc[hh] = 0.f;
 #pragma unroll
-        for (int j = 0; j < DI; ++j)
-            acc = fmaf(to_f32(qb[hh * DI + j]), k[j], acc);
-        if (valid)
-            put_score(a, row0 + hh, t, acc);
+        for (int p = 0; p < DI / EPC; ++p) {
+            T q[EPC];
+            __builtin_memcpy(q, &qv[hh][p], 16);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+                acc[hh] = fmaf(to_f32(q[e]), k[p * EPC + e], acc[hh]);
+        }
     }
+    if (valid)
+#pragma unroll
+        for (int hh = 0; hh < GI; ++hh)
+            put_score(a, row0 + hh, t, acc[hh]);
 }
 
 template <typename T, int D, int DI, int GI>
@@ -175,6 +200,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
     const bool valid = t < t_new;
 
     constexpr int EPC = 16 / sizeof(T);
+    uint4 qv[GI][DI * sizeof(T) / 16];
+    load_queries<T, DI, GI>(a, b, g, qv);
     float k[DI];
     {
         const T *row = (const T *)a.kp + (((size_t)b * a.Hkv + g) * a.cap + (valid ? t : t0)) * DI;
@@ -188,7 +215,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
                 k[p * EPC + e] = to_f32(v[e]);
         }
     }
-    score_heads<T, DI, GI>(a, b, g, t, k, valid);
+    score_heads<T, DI, GI>(a, b, g, t, k, valid, qv);
 }
 
 template <typename T, int D, int DI, int GI>
