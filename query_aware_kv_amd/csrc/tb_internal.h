@@ -88,6 +88,20 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Work-group barrier for LDS traffic only: each wave's LDS operations have
+// completed when it arrives and the compiler moves no memory access across
+// it, but global loads still in flight are not waited for.  (__syncthreads
+// would wait for them: its fences must cover global stores, and on this
+// architecture one counter tracks global loads and stores together.)  Only
+// for phases that communicate through LDS alone.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- wave ops
 // Cross-lane steps through DPP row permutations (no LDS round trip); out of
 // row sources read 0.

@@ -268,23 +268,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // m = 4 tid .. 4 tid + 3) and its word's 32 keys are requested before
     // the context length is known, the sample first so that its histogram
     // can be built while the keys arrive (masked by position afterwards).
+    // The loads are unconditional, at clamped addresses (so that the
+    // compiler can wait for the sample alone): a thread past the row reads
+    // the row's last word again, and a row's partial last word may read up
+    // to 62 bytes past the row, which stays inside the workspace (the
+    // compact sample follows the keys).
     uint2 s16v = make_uint2(0u, 0u);
     uint4 k16v[4] = {};
-    const bool k16vec = K16 && (cap & 7) == 0 && 32 * tid + 32 <= cap;
+    const bool k16vec = K16 && (cap & 7) == 0;
     if constexpr (K16) {
-        if (4 * tid < s16)
-            s16v = *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + 4 * tid);
-        if (k16vec) {
-            const uint4 *src = reinterpret_cast<const uint4 *>(keys16 + rowid * cap + 32 * tid);
+        const int ms = 4 * tid < s16 ? 4 * tid : s16 - 4;
+        s16v = *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + ms);
+        // (rows that do not start 16-byte aligned read the buffer's aligned
+        // start instead, unused: no branch, so the waits stay exact)
+        const int wl = (cap + 31) / 32 - 1;
+        const uint4 *src = reinterpret_cast<const uint4 *>(
+            k16vec ? keys16 + rowid * cap + 32 * (tid < wl ? tid : wl) : keys16);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                k16v[q] = src[q];
-        }
+        for (int q = 0; q < 4; ++q)
+            k16v[q] = src[q];
     }
     const int n = clamp_len(ctx_len[b], cap);
-    if (keep_from != nullptr && i == 0 && tid == 0)
-        keep_from[b] = n - n_new > 0 ? n - n_new : 0;
     if (n == 0) {
+        if (keep_from != nullptr && i == 0 && tid == 0)
+            keep_from[b] = 0;
         if (tid == 0)
             sel_count[rowid] = 0;
         if (sel_bits != nullptr)
@@ -377,7 +384,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (sampled)
             for (int e = tid; e < kSampleBins; e += kSelThreads)
                 shist[e] = 0u;
-        __syncthreads();
+        // (the 16-bit keys may still be arriving: only LDS is synchronised
+        // until the classification pass)
+        lds_barrier();
         bool found = false;
         if (sampled) {
             // ---- bracket tau from the keys at positions 8m ----
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     if (s4[q] != 0u)
                         atomicAdd(&shist[s4[q] >> kBinShift], 1u);
             }
-            __syncthreads();
+            lds_barrier();
             if (wave == 0) {
                 // sample ranks a margin either side of the expected rank of tau
                 const BinScan sc(shist, lane);
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     misc[5] = b_hi;
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // candidate range [plo, phim1]: bins b_lo .. b_hi; keys above are
             // kept.  Candidates are also counted by their top 20 bits (bin and
             // the next 8 bits) when their bins are few enough for that.
@@ -507,14 +516,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                         kw[4 * q + 3] = k16v[q].w;
                     }
                 } else {
-                    const uint16_t *src = keys16 + rowid * cap + 32 * tid;
+                    // one 16-bit key at a time, every load issued first (a
+                    // position past the row reads its last key; masked below)
+                    const uint16_t *src = keys16 + rowid * cap;
+                    uint32_t h[32];
 #pragma unroll
-                    for (int e2 = 0; e2 < 16; ++e2) {
-                        const int p = 32 * tid + 2 * e2;
-                        const uint32_t a0 = p < n ? src[2 * e2] : 0u;
-                        const uint32_t a1 = p + 1 < n ? src[2 * e2 + 1] : 0u;
-                        kw[e2] = a0 | (a1 << 16);
+                    for (int e = 0; e < 32; ++e) {
+                        const int p = 32 * tid + e;
+                        h[e] = src[p < cap ? p : cap - 1];
                     }
+#pragma unroll
+                    for (int e2 = 0; e2 < 16; ++e2)
+                        kw[e2] = h[2 * e2] | (h[2 * e2 + 1] << 16);
                 }
                 uint32_t wt = 0u, wc = 0u;
 #pragma unroll
@@ -634,6 +647,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             need = krem;
         }
     }
+    // (stored late: an early store would make the first loads' waits
+    // conservative)
+    if (keep_from != nullptr && i == 0 && tid == 0)
+        keep_from[b] = n - n_new > 0 ? n - n_new : 0;
     // Kept: every valid key with (key & fmask) >= thr (every valid key when
     // thr is 0, none when none_kept).  With split ties the keys with
     // (key & fmask) == tau are ties, need of them kept, lowest positions first.
