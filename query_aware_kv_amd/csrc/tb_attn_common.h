@@ -181,7 +181,8 @@ __device__ __forceinline__ void arrive_and_combine(CombineLds<GQ, THREADS, NCH> 
         const int cc = part + r * NPART;
         v0[r] = load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
     }
-    __syncthreads();
+    // the (max, sum) pairs are in LDS; the partial sums stay in flight
+    lds_barrier();
     for (int hl = wave; hl < GQ; hl += NWAVES) {
         float M = -INFINITY;
         for (int cc = lane; cc < nact; cc += 64)
