@@ -167,7 +167,8 @@ struct WsLayout {
     size_t part_o;   // attention partial sums [b][Hq][nchunk][D] fp32
     size_t part_ml;  // attention partial (max, sum) [b][Hq][nchunk][2] fp32
     size_t counters; // attention arrival counters [b][Hkv] u32 (kept zero)
-    size_t keys16;   // top 16 bits of each score's key [b][Himp][cap] u16 (fused step)
+    size_t keys16;   // top 16 bits of each score's key [b][Himp][keys16_stride] u16,
+                     // in pair order (fused step)
     size_t sample16; // the same for positions 8m, compact [b][Himp][sample16_stride] u16
     size_t total;
 };
@@ -178,6 +179,15 @@ inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 inline int dense_chunks(int cap) { return (cap + kDenseChunk - 1) / kDenseChunk; }
 // u16 entries per row of the compact sample (positions 8m), a multiple of 8
 inline int sample16_stride(int cap) { return ((cap + 7) / 8 + 7) & ~7; }
+// u16 entries per row of the 16-bit keys: whole 32-position words.  Within
+// word w the key of position 32w + j (j < 16) is entry 32w + 2j and that of
+// position 32w + 16 + j is entry 32w + 2j + 1, so that the 32-bit pair j
+// holds bits j and 16 + j of the word's membership masks.
+inline int keys16_stride(int cap) { return (cap + 31) & ~31; }
+__host__ __device__ inline int keys16_entry(int t)
+{
+    return (t & ~31) | ((t & 15) << 1) | ((t >> 4) & 1);
+}
 // Chunk partials are laid out per kernel's own chunk count; the region fits
 // the larger of the two.
 inline int max_chunks(int cap)
@@ -199,7 +209,8 @@ inline WsLayout ws_layout(const tb_shape &s)
     L.counters = off;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
     L.keys16 = off;
-    off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(uint16_t));
+    off += align_up((size_t)s.batch * s.n_imp_heads * keys16_stride(s.ctx_cap) *
+                    sizeof(uint16_t));
     L.sample16 = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * sample16_stride(s.ctx_cap) *
                     sizeof(uint16_t));
@@ -219,8 +230,9 @@ hipError_t launch_append_project(const tb_shape &s, const void *k_new, const voi
 // and scores them.
 int score_max_fused_new();
 // When keys16 is not NULL the launch also stores the top 16 bits of every
-// score's key into keys16[row][t] and, for positions t = 8m, into
-// sample16[row][m] (row stride sample16_stride(cap)).
+// score's key into keys16[row][keys16_entry(t)] (row stride
+// keys16_stride(cap)) and, for positions t = 8m, into sample16[row][m] (row
+// stride sample16_stride(cap)).
 hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
                         const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
                         const void *v_new, const void *w, void *k_cache, void *v_cache,

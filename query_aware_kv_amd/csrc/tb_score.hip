@@ -44,9 +44,9 @@ struct ScoreArgs {
     const void *k_new, *v_new; // [b][Hkv][n_new][D]
     const void *w;             // [D][d]
     void *k_cache, *v_cache;
-    uint16_t *keys16;   // [b][Himp][cap] top 16 key bits of every score, or NULL
+    uint16_t *keys16;   // [b][Himp][k16s] top 16 key bits of every score (pair order), or NULL
     uint16_t *sample16; // [b][Himp][s16] the same for positions 8m
-    int s16;
+    int s16, k16s;
 };
 
 // Stores the score of (row, t) and, when asked, its 16-bit key.
@@ -55,7 +55,7 @@ __device__ __forceinline__ void put_score(const ScoreArgs &a, size_t row, int t,
     a.scores[row * a.cap + t] = v;
     if (a.keys16 != nullptr) {
         const uint16_t k16 = (uint16_t)(score_key(v) >> 16);
-        a.keys16[row * a.cap + t] = k16;
+        a.keys16[row * a.k16s + keys16_entry(t)] = k16;
         if ((t & 7) == 0)
             a.sample16[row * a.s16 + (t >> 3)] = k16;
     }
@@ -277,6 +277,7 @@ hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
     a.keys16 = keys16;
     a.sample16 = sample16;
     a.s16 = sample16_stride(s.ctx_cap);
+    a.k16s = keys16_stride(s.ctx_cap);
     if (s.dtype == TB_BF16)
         return score_dtype<bf16_t>(s, a, st);
     return score_dtype<float>(s, a, st);

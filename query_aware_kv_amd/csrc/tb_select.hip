@@ -192,6 +192,20 @@ struct BinScan {
     }
 };
 
+// Packed unsigned 16-bit saturating subtract and minimum (two keys per op).
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b)
+{
+    uint32_t d;
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 // Loads the 32 keys of bitmap word w.  Only positions in [lo, hi) (the
 // middle region between the sink and the local window, hi <= n) compete for
 // the budget; every other position gets key 0.  Whole words of 16-byte
@@ -268,22 +282,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // m = 4 tid .. 4 tid + 3) and its word's 32 keys are requested before
     // the context length is known, the sample first so that its histogram
     // can be built while the keys arrive (masked by position afterwards).
-    // The loads are unconditional, at clamped addresses (so that the
-    // compiler can wait for the sample alone): a thread past the row reads
-    // the row's last word again, and a row's partial last word may read up
-    // to 62 bytes past the row, which stays inside the workspace (the
-    // compact sample follows the keys).
+    // The keys come in whole words of 64 bytes (rows of keys16_stride(cap)
+    // entries, pair order), so every load is a 16-byte one.  The loads are
+    // unconditional, at clamped addresses (so that the compiler can wait for
+    // the sample alone): a thread past the row reads the row's last word
+    // again.
     uint2 s16v = make_uint2(0u, 0u);
     uint4 k16v[4] = {};
-    const bool k16vec = K16 && (cap & 7) == 0;
     if constexpr (K16) {
         const int ms = 4 * tid < s16 ? 4 * tid : s16 - 4;
         s16v = *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + ms);
-        // (rows that do not start 16-byte aligned read the buffer's aligned
-        // start instead, unused: no branch, so the waits stay exact)
-        const int wl = (cap + 31) / 32 - 1;
+        const int wl = (cap + 31) / 32 - 1; // the row's last word
         const uint4 *src = reinterpret_cast<const uint4 *>(
-            k16vec ? keys16 + rowid * cap + 32 * (tid < wl ? tid : wl) : keys16);
+            keys16 + rowid * (size_t)(32 * (wl + 1)) + 32 * (tid < wl ? tid : wl));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             k16v[q] = src[q];
@@ -505,39 +516,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 }
             };
             if constexpr (K16) {
-                // this thread's word from the 16-bit keys: bin = key16 >> 4
-                uint32_t kw[16];
-                if (k16vec) {
+                // this thread's word from its 16 key pairs (pair j: the
+                // 16-bit keys of positions 32 tid + j and 32 tid + 16 + j),
+                // two keys per packed op: a key's 12-bit bin is key16 >> 4,
+                // so bin > b_hi is key16 >= kt and bin < b_lo is key16 < kl.
+                // sat(kt - key16) is nonzero iff the key is not above the
+                // range, sat(kl - key16) iff it is below; min(., 1) turns
+                // each into the word's bit j (low half) or 16 + j (high half).
+                const uint32_t kw[16] = {k16v[0].x, k16v[0].y, k16v[0].z, k16v[0].w,
+                                         k16v[1].x, k16v[1].y, k16v[1].z, k16v[1].w,
+                                         k16v[2].x, k16v[2].y, k16v[2].z, k16v[2].w,
+                                         k16v[3].x, k16v[3].y, k16v[3].z, k16v[3].w};
+                const uint32_t kt = b_hi + 1u < 4096u ? (b_hi + 1u) << 4 : 0xFFFFu;
+                const uint32_t ktv = kt * 0x10001u, klv = (b_lo << 4) * 0x10001u;
+                uint32_t not_above = 0u, below = 0u;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        kw[4 * q + 0] = k16v[q].x;
-                        kw[4 * q + 1] = k16v[q].y;
-                        kw[4 * q + 2] = k16v[q].z;
-                        kw[4 * q + 3] = k16v[q].w;
-                    }
-                } else {
-                    // one 16-bit key at a time, every load issued first (a
-                    // position past the row reads its last key; masked below)
-                    const uint16_t *src = keys16 + rowid * cap;
-                    uint32_t h[32];
-#pragma unroll
-                    for (int e = 0; e < 32; ++e) {
-                        const int p = 32 * tid + e;
-                        h[e] = src[p < cap ? p : cap - 1];
-                    }
-#pragma unroll
-                    for (int e2 = 0; e2 < 16; ++e2)
-                        kw[e2] = h[2 * e2] | (h[2 * e2 + 1] << 16);
+                for (int j = 0; j < 16; ++j) {
+                    not_above |= pk_min_u16(pk_sub_sat_u16(ktv, kw[j]), 0x10001u) << j;
+                    below |= pk_min_u16(pk_sub_sat_u16(klv, kw[j]), 0x10001u) << j;
                 }
-                uint32_t wt = 0u, wc = 0u;
-#pragma unroll
-                for (int e = 0; e < 32; ++e) {
-                    const int p = 32 * tid + e;
-                    const uint32_t bin = ((kw[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) >> 4;
-                    const bool valid = p < n && p >= lo && p < hi;
-                    wt |= (uint32_t)(valid && bin > b_hi) << e;
-                    wc |= (uint32_t)(valid && bin >= b_lo && bin <= b_hi) << e;
-                }
+                // valid: positions of the middle region [lo, hi)
+                const uint32_t vm = mask_below(tid, hi) & ~mask_below(tid, lo);
+                // (with b_hi the top bin no key is above the range)
+                const uint32_t wt = b_hi + 1u < 4096u ? ~not_above & vm : 0u;
+                const uint32_t wc = not_above & ~below & vm;
                 pass_word(tid, wt, wc);
             } else {
                 for_words([&](int w, const auto &k) {
