@@ -61,6 +61,7 @@ static_assert(kSampleBins == 64 * 64 && (1u << (32 - kBinShift)) == kSampleBins,
 static_assert(kSampleBins <= kCopies * kCopyStride, "sample histogram reuses the radix one");
 // misc words
 constexpr int kMiscScan = 8;   // kSelWaves + 1 words of block-scan scratch
+constexpr int kMiscList = 40;  // length of the list of keys sharing tau's 20-bit prefix
 
 // Exclusive scan of popcount(words[w]) over w < nw into out[w] (skipped when
 // out is NULL); returns the total to every thread.  wsum: kSelWaves words of
@@ -160,10 +161,12 @@ struct BinScan {
     int lane;
     __device__ BinScan(const uint32_t *hist, int lane_) : h(hist), lane(lane_)
     {
+        // (each lane starts its 16 reads at its own rotation, so that the
+        // lanes of one read, 256 bytes apart, fall into different banks)
         uint32_t s = 0u;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            const uint4 v = reinterpret_cast<const uint4 *>(hist)[lane * 16 + c];
+            const uint4 v = reinterpret_cast<const uint4 *>(hist)[lane * 16 + ((c + lane) & 15)];
             s += v.x + v.y + v.z + v.w;
         }
         ls = s;
@@ -188,7 +191,8 @@ struct BinScan {
     {
 #pragma unroll
         for (int c = 0; c < 16; ++c)
-            reinterpret_cast<uint4 *>(hist)[lane_ * 16 + c] = make_uint4(0u, 0u, 0u, 0u);
+            reinterpret_cast<uint4 *>(hist)[lane_ * 16 + ((c + lane_) & 15)] =
+                make_uint4(0u, 0u, 0u, 0u);
     }
 };
 
@@ -572,50 +576,105 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 if (wave == 0) {
                     const BinScan sc(hist, lane);
                     const BinHit h = sc.find((uint32_t)B - A - 1u);
-                    sc.clear(hist, lane);
                     if (lane == 0) {
                         misc[0] = d0 + h.bin;          // 20-bit prefix of tau
                         misc[1] = (uint32_t)B - A - h.above; // rank inside it
+                        misc[2] = h.count;             // candidates with that prefix
                     }
                 }
                 __syncthreads();
-                const uint32_t p20 = misc[0];
-                for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
-                    if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
-                        const uint32_t kc = cpair[i].x;
-                        if ((kc >> 12) == p20)
-                            atomicAdd(&hist[kc & 4095u], 1u);
+                const uint32_t p20 = misc[0], krem = misc[1], m20 = misc[2];
+                if (m20 <= 64u) {
+                    // Few keys share the prefix (the usual case): candidates
+                    // above it are kept now, each wave taking its own, and
+                    // those with it gather in a list that one wave ranks.
+                    uint2 *tl = reinterpret_cast<uint2 *>(tot + 64);
+                    const uint32_t tw = tot[wave];
+                    for (uint32_t e = lane; e < tw; e += 64) {
+                        const uint2 c = cwave[e];
+                        const uint32_t pf = c.x >> 12;
+                        if (pf > p20)
+                            atomicOr(&Tb[c.y >> 5], 1u << (c.y & 31u));
+                        else if (pf == p20)
+                            tl[atomicAdd(&misc[kMiscList], 1u)] = c;
                     }
-                }
-                __syncthreads();
-                if (wave == 0) {
-                    const uint32_t krem = misc[1];
-                    const BinScan sc(hist, lane);
-                    const BinHit h = sc.find(krem - 1u);
-                    if (lane == 0) {
-                        misc[2] = (p20 << 12) | h.bin; // tau
-                        misc[3] = krem - h.above;      // ties at tau kept
-                        misc[6] = h.count;             // keys equal to tau
+                    __syncthreads();
+                    if (wave == 0) {
+                        // tau is the key with (keys above) < krem <= (keys
+                        // above or equal) among the m20 listed keys
+                        const uint2 c = tl[lane < (int)m20 ? lane : 0];
+                        uint32_t above = 0u, eq = 0u;
+                        for (uint32_t j = 0; j < m20; ++j) {
+                            const uint32_t kj = __builtin_amdgcn_readlane(c.x, j);
+                            above += kj > c.x ? 1u : 0u;
+                            eq += kj == c.x ? 1u : 0u;
+                        }
+                        const bool hit = lane < (int)m20 && above < krem && krem <= above + eq;
+                        const int x = __ffsll(__ballot(hit)) - 1;
+                        const uint32_t t = __builtin_amdgcn_readlane(c.x, x);
+                        const uint32_t nd = krem - __builtin_amdgcn_readlane(above, x);
+                        const uint32_t ce = __builtin_amdgcn_readlane(eq, x);
+                        // the listed keys at or above tau join the kept
+                        // words; those equal to it are ties when ties split
+                        if (lane < (int)m20) {
+                            const uint32_t bit = 1u << (c.y & 31u);
+                            if (c.x > t || (c.x == t && nd >= ce))
+                                atomicOr(&Tb[c.y >> 5], bit);
+                            else if (c.x == t)
+                                atomicOr(&Sb[c.y >> 5], bit);
+                        }
+                        if (lane == 0) {
+                            misc[3] = t;  // tau
+                            misc[6] = nd; // ties at tau kept
+                            misc[7] = ce; // keys equal to tau
+                        }
                     }
-                }
-                __syncthreads();
-                tau = misc[2];
-                need = misc[3];
-                cnt_eq = misc[6];
-                // candidates at or above tau join the kept words; those equal
-                // to tau are ties when ties are split
-                const bool split = need < cnt_eq;
-                for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
-                    if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
-                        const uint2 c = cpair[i];
-                        const uint32_t bit = 1u << (c.y & 31u);
-                        if (c.x > tau || (c.x == tau && !split))
-                            atomicOr(&Tb[c.y >> 5], bit);
-                        else if (c.x == tau)
-                            atomicOr(&Sb[c.y >> 5], bit);
+                    __syncthreads();
+                    tau = misc[3];
+                    need = misc[6];
+                    cnt_eq = misc[7];
+                } else {
+                    // many keys share the prefix: a histogram of their low
+                    // 12 bits finds tau, then every candidate is placed
+                    for (int e = tid; e < kSampleBins; e += kSelThreads)
+                        hist[e] = 0u;
+                    __syncthreads();
+                    for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                        if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
+                            const uint32_t kc = cpair[i].x;
+                            if ((kc >> 12) == p20)
+                                atomicAdd(&hist[kc & 4095u], 1u);
+                        }
                     }
+                    __syncthreads();
+                    if (wave == 0) {
+                        const BinScan sc(hist, lane);
+                        const BinHit h = sc.find(krem - 1u);
+                        if (lane == 0) {
+                            misc[3] = (p20 << 12) | h.bin; // tau
+                            misc[6] = krem - h.above;      // ties at tau kept
+                            misc[7] = h.count;             // keys equal to tau
+                        }
+                    }
+                    __syncthreads();
+                    tau = misc[3];
+                    need = misc[6];
+                    cnt_eq = misc[7];
+                    // candidates at or above tau join the kept words; those
+                    // equal to tau are ties when ties are split
+                    const bool split = need < cnt_eq;
+                    for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                        if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
+                            const uint2 c = cpair[i];
+                            const uint32_t bit = 1u << (c.y & 31u);
+                            if (c.x > tau || (c.x == tau && !split))
+                                atomicOr(&Tb[c.y >> 5], bit);
+                            else if (c.x == tau)
+                                atomicOr(&Sb[c.y >> 5], bit);
+                        }
+                    }
+                    __syncthreads();
                 }
-                __syncthreads();
                 emitted = true;
             } else {
                 for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)

@@ -328,6 +328,8 @@ def _long_rows(kind, bsz, H, cap, seed):
         return g * 5.0
     if kind == "levels":        # 4096 distinct values: ties at the threshold
         return np.floor(g * 512.0).astype(np.float32)
+    if kind == "coarse":        # steps of 1/32: about 180 keys share the threshold's value
+        return (np.floor(g * 32.0) / 32.0).astype(np.float32)
     if kind == "sample_low":    # every eighth position far below the rest
         g[..., ::8] -= 100.0
         return g
@@ -341,8 +343,8 @@ def _long_rows(kind, bsz, H, cap, seed):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("kind", ["gauss", "levels", "sample_low", "sample_high", "narrow",
-                                  "equal"])
+@pytest.mark.parametrize("kind", ["gauss", "levels", "coarse", "sample_low", "sample_high",
+                                  "narrow", "equal"])
 @pytest.mark.parametrize("cap,lens", [(32768, [32768, 20001, 2049]), (70000, [70000, 40000])])
 def test_select_long_rows(kind, cap, lens):
     # long rows go through the sampled bracket of the threshold when it holds
