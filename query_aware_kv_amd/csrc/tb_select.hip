@@ -491,32 +491,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 const uint32_t inc = wave_incl_scan(c, lane);
                 uint32_t slot = run + inc - c;
                 run += __builtin_amdgcn_readlane(inc, 63);
-                // the few candidate keys are re-read (from cache), eight
-                // loads in flight at a time
+                // this lane's candidate positions, in slot order (their keys
+                // are read below, the wave's lanes sharing the reads evenly)
                 while (wc) {
-                    int pos[8];
-                    bool ok[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        ok[t] = wc != 0u;
-                        pos[t] = w * 32 + (ok[t] ? __ffs(wc) - 1 : 0);
-                        wc &= wc - 1u;
-                    }
-                    float f[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        f[t] = row[pos[t]];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        if (ok[t]) {
-                            const uint32_t kc = score_key(f[t]);
-                            if (slot < (uint32_t)kWaveCap)
-                                cwave[slot] = make_uint2(kc, (uint32_t)pos[t]);
-                            ++slot;
-                            if (lvl)
-                                atomicAdd(&hist[(kc >> 12) - d0], 1u);
-                        }
-                    }
+                    if (slot < (uint32_t)kWaveCap)
+                        cwave[slot].y = (uint32_t)(w * 32 + __ffs(wc) - 1);
+                    ++slot;
+                    wc &= wc - 1u;
                 }
             };
             if constexpr (K16) {
@@ -555,6 +536,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     }
                     pass_word(w, wt, wc);
                 });
+            }
+            {
+                // the wave's candidate keys, re-read (from cache) with every
+                // lane taking an equal share and all requests in flight
+                // together; the positions were written by this wave only
+                __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0)
+                __builtin_amdgcn_wave_barrier();
+                const uint32_t nc = run < (uint32_t)kWaveCap ? run : (uint32_t)kWaveCap;
+                for (uint32_t e0 = 0; e0 < nc; e0 += 4 * 64) {
+                    uint32_t pos[4];
+                    float f[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t e = e0 + 64 * t + lane;
+                        pos[t] = e < nc ? cwave[e].y : 0u;
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        f[t] = row[pos[t]];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const uint32_t e = e0 + 64 * t + lane;
+                        if (e < nc) {
+                            const uint32_t kc = score_key(f[t]);
+                            cwave[e].x = kc;
+                            if (lvl)
+                                atomicAdd(&hist[(kc >> 12) - d0], 1u);
+                        }
+                    }
+                }
             }
             na = wave_reduce(na, [](uint32_t x, uint32_t y) { return x + y; });
             if (lane == 0) {
