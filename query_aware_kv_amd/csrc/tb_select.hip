@@ -302,7 +302,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             k16v[q] = src[q];
+        // A use on a path never taken (the budget is never negative) keeps
+        // these requests ahead of the first branch; otherwise they would
+        // be moved below the early exit, after the context length arrives.
+        if (B < 0)
+            sel_count[rowid] = (int32_t)(s16v.x ^ k16v[0].x ^ k16v[1].x ^ k16v[2].x ^ k16v[3].x);
     }
+    // LDS that starts at zero (radix and sample histograms, misc words),
+    // cleared before anything depends on the context length
+    for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+        hist[e] = 0u;
+    for (int e = tid; e < kSampleBins; e += kSelThreads)
+        reinterpret_cast<uint32_t *>(cpair)[e] = 0u;
+    if (tid < 64)
+        misc[tid] = 0u;
     const int n = clamp_len(ctx_len[b], cap);
     if (n == 0) {
         if (keep_from != nullptr && i == 0 && tid == 0)
@@ -321,8 +334,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     // budget goes to the middle region [lo, hi)
     const int lo = n_sink < n ? n_sink : n;
     const int hi = n_local < n - lo ? n - n_local : lo;
-    if (tid < 64)
-        misc[tid] = 0u;
 
     // full keys live in registers with one word per thread (not needed when
     // the first pass reads the 16-bit keys)
@@ -394,11 +405,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         // written before the histogram has been read.
         uint32_t *shist = reinterpret_cast<uint32_t *>(cpair);
         const bool sampled = nw >= kMinSampleWords;
-        for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
-            hist[e] = 0u;
-        if (sampled)
-            for (int e = tid; e < kSampleBins; e += kSelThreads)
-                shist[e] = 0u;
         // (the 16-bit keys may still be arriving: only LDS is synchronised
         // until the classification pass)
         lds_barrier();
