@@ -73,6 +73,7 @@ struct AttnArgs {
     const int32_t *keep_from;
     const int32_t *ctx_len;
     int Hq, Hkv, Himp, cap;
+    int q_per_imp_log2; // log2(Hq / Himp)
     float qscale;
     float *part_o;     // [b*Hq][nchunk][D]
     float *part_ml;    // [b*Hq][nchunk][2]
@@ -122,10 +123,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int p0w = c0 + 32 * (wpart * WPW + lane); // first position of this lane's word
     uint32_t word = 0u;
     if constexpr (BITMAP) {
-        if (lane < WPW && p0w < a.cap) {
-            const int i = (int)((long)(g * GQ + hw) * a.Himp / a.Hq);
-            word = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride + (p0w >> 5)];
-        }
+        // query head h follows importance head h / (Hq / Himp), a power-of-two
+        // ratio; the load is unconditional (a word past the row reads the
+        // row's first) and masked afterwards
+        const int i = (g * GQ + hw) >> a.q_per_imp_log2;
+        const uint32_t wv = a.sel_bits[((size_t)b * a.Himp + i) * a.bits_stride +
+                                       (p0w < a.cap ? p0w >> 5 : 0)];
+        word = wv & (0u - (uint32_t)(lane < WPW && p0w < a.cap));
     }
     const int kf_raw = a.keep_from != nullptr ? a.keep_from[b] : a.cap;
     const int n = clamp_len(a.ctx_len[b], a.cap);
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             __syncthreads();
             for (int hl = wave; hl < GQ; hl += kAttnWaves) {
                 const int h = g * GQ + hl;
-                const int i = (int)((long)h * a.Himp / a.Hq);
+                const int i = h >> a.q_per_imp_log2;
                 const size_t li = (size_t)b * a.Himp + i;
                 const int32_t *L = a.sel_idx + li * a.sel_stride;
                 int cnt = a.sel_count[li];
@@ -336,6 +340,9 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
     a.Hkv = s.n_kv_heads;
     a.Himp = s.n_imp_heads;
     a.cap = s.ctx_cap;
+    a.q_per_imp_log2 = 0;
+    while ((s.n_imp_heads << a.q_per_imp_log2) < s.n_q_heads)
+        ++a.q_per_imp_log2;
     a.qscale = softmax_scale * 1.4426950408889634f; // logits in base 2
     a.part_o = part_o;
     a.part_ml = part_ml;
