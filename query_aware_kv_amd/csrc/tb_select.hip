@@ -98,6 +98,25 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
 }
 
 // Writes the positions of the set bits of words[0..nw) in ascending order.
+// Set bits over nw words, the whole work-group (one barrier; wsum:
+// kSelWaves words, not reused afterwards).
+__device__ uint32_t block_popc_total(const uint32_t *words, int nw, uint32_t *wsum)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t local = 0u;
+    for (int w = tid; w < nw; w += kSelThreads)
+        local += __popc(words[w]);
+    const uint32_t t = wave_reduce(local, [](uint32_t x, uint32_t y) { return x + y; });
+    if (lane == 0)
+        wsum[wave] = t;
+    __syncthreads();
+    uint32_t total = 0u;
+#pragma unroll
+    for (int v = 0; v < kSelWaves; ++v)
+        total += wsum[v];
+    return total;
+}
+
 __device__ void compact_bits(const uint32_t *words, const uint32_t *offs, int nw, int32_t *dst)
 {
     for (int w = threadIdx.x; w < nw; w += kSelThreads) {
@@ -830,8 +849,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
 
     // ---- |S|, the ascending list (when asked) and the bitmap (when asked) ----
-    const uint32_t total =
-        block_popc_exscan(fin, sel_idx != nullptr ? scan : nullptr, nw, misc + kMiscScan);
+    const uint32_t total = sel_idx != nullptr
+                               ? block_popc_exscan(fin, scan, nw, misc + kMiscScan)
+                               : block_popc_total(fin, nw, misc + kMiscScan);
     if (sel_idx != nullptr)
         compact_bits(fin, scan, nw, sel_idx + rowid * sel_stride);
     if (sel_bits != nullptr)
