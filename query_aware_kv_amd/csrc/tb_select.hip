@@ -518,9 +518,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 run += __builtin_amdgcn_readlane(inc, 63);
                 // this lane's candidate positions, in slot order (their keys
                 // are read below, the wave's lanes sharing the reads evenly)
+                // (past the wave's capacity the last slot is overwritten:
+                // the selection then takes the full radix path, which does
+                // not read the candidates)
                 while (wc) {
-                    if (slot < (uint32_t)kWaveCap)
-                        cwave[slot].y = (uint32_t)(w * 32 + __ffs(wc) - 1);
+                    cwave[slot < (uint32_t)kWaveCap ? slot : (uint32_t)kWaveCap - 1u].y =
+                        (uint32_t)(w * 32 + __ffs(wc) - 1);
                     ++slot;
                     wc &= wc - 1u;
                 }
@@ -574,21 +577,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     float f[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
+                        // (every lane reads a slot, masked after: no branch
+                        // between the reads)
                         const uint32_t e = e0 + 64 * t + lane;
-                        pos[t] = e < nc ? cwave[e].y : 0u;
+                        const uint32_t pv = cwave[e < nc ? e : 0u].y;
+                        pos[t] = pv & (0u - (uint32_t)(e < nc));
                     }
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         f[t] = row[pos[t]];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
+                        // the key is stored by every lane (past the list
+                        // into a word of its own in the prefix-list area,
+                        // written only later), so no branch holds the loads
                         const uint32_t e = e0 + 64 * t + lane;
-                        if (e < nc) {
-                            const uint32_t kc = score_key(f[t]);
-                            cwave[e].x = kc;
-                            if (lvl)
-                                atomicAdd(&hist[(kc >> 12) - d0], 1u);
-                        }
+                        const uint32_t kc = score_key(f[t]);
+                        *(e < nc ? &cwave[e < nc ? e : 0u].x : &tot[64 + lane]) = kc;
+                        if (lvl && e < nc)
+                            atomicAdd(&hist[(kc >> 12) - d0], 1u);
                     }
                 }
             }
