@@ -304,12 +304,15 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                                             a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
                                             st)));
     if (a->refresh) {
+        // the 16-bit keys and their sample only where the selection reads them
+        const bool k16 = select_key16(shape->ctx_cap);
         TB_TRY(hip_rc(launch_score(*shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
                                    fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
-                                   a->k_cache, a->v_cache, W.keys16, W.sample16, st)));
+                                   a->k_cache, a->v_cache, k16 ? W.keys16 : nullptr,
+                                   k16 ? W.sample16 : nullptr, st)));
         TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
                                     a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
-                                    W.keys16, W.sample16, st)));
+                                    k16 ? W.keys16 : nullptr, k16 ? W.sample16 : nullptr, st)));
     }
     return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
                               a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,

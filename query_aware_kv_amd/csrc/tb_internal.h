@@ -184,6 +184,9 @@ inline int sample16_stride(int cap) { return ((cap + 7) / 8 + 7) & ~7; }
 // position 32w + 16 + j is entry 32w + 2j + 1, so that the 32-bit pair j
 // holds bits j and 16 + j of the word's membership masks.
 inline int keys16_stride(int cap) { return (cap + 31) & ~31; }
+// The selection's first pass reads the 16-bit keys when a row is at most one
+// 32-position word per selection thread (1024 words).
+inline bool select_key16(int cap) { return (cap + 31) / 32 <= 1024; }
 __host__ __device__ inline int keys16_entry(int t)
 {
     return (t & ~31) | ((t & 15) << 1) | ((t >> 4) & 1);

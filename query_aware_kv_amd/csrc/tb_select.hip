@@ -44,6 +44,8 @@
 //      bitmap itself can be written out too.
 #include "tb_internal.h"
 
+#include <atomic>
+
 
 namespace tb {
 namespace {
@@ -868,6 +870,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         sel_count[rowid] = (int32_t)total;
 }
 
+// words per bitmap array, even so that the candidate pairs stay 8-byte aligned
+inline int sel_words(int cap) { return ((cap + 31) / 32 + 2) & ~1; }
+// dynamic LDS of one selection work-group
+inline size_t sel_lds_bytes(int cap)
+{
+    const size_t nwc = (size_t)sel_words(cap);
+    const size_t u = 2 * nwc > 2 * (size_t)kSelWaves * kWaveCap ? 2 * nwc
+                                                                 : 2 * (size_t)kSelWaves * kWaveCap;
+    return ((size_t)kCopies * kCopyStride + 256 + 64 + 2 * nwc + u) * sizeof(uint32_t);
+}
+
 template <int WPT, bool K16>
 hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
@@ -875,18 +888,25 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
                     int32_t *keep_from, int n_new, const uint16_t *keys16,
                     const uint16_t *sample16, hipStream_t st)
 {
-    // words per bitmap array, even so that the candidate pairs stay 8-byte aligned
-    const int nwc = ((s.ctx_cap + 31) / 32 + 2) & ~1;
-    const size_t u = 2 * (size_t)nwc > 2 * (size_t)kSelWaves * kWaveCap
-                         ? 2 * (size_t)nwc
-                         : 2 * (size_t)kSelWaves * kWaveCap;
-    const size_t lds = ((size_t)kCopies * kCopyStride + 256 + 64 + 2 * (size_t)nwc + u) *
-                       sizeof(uint32_t);
+    const int nwc = sel_words(s.ctx_cap);
+    const size_t lds = sel_lds_bytes(s.ctx_cap);
     if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)select_kernel<WPT, K16>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        // the launch limit is raised once per device, to what the largest
+        // capacity needs
+        static std::atomic<uint64_t> raised{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess)
             return e;
+        const uint64_t bit = dev < 64 ? 1ull << dev : 0ull;
+        if (bit == 0ull || (raised.load(std::memory_order_relaxed) & bit) == 0ull) {
+            e = hipFuncSetAttribute((const void *)select_kernel<WPT, K16>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)sel_lds_bytes(kMaxCtxCap));
+            if (e != hipSuccess)
+                return e;
+            raised.fetch_or(bit, std::memory_order_relaxed);
+        }
     }
     dim3 grid(s.n_imp_heads, s.batch);
     hipLaunchKernelGGL((select_kernel<WPT, K16>), grid, dim3(kSelThreads), lds, st, scores,
@@ -908,7 +928,8 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
 #define TB_SEL_ARGS                                                                          \
     s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from,       \
         n_new, keys16, sample16, st
-    if ((s.ctx_cap + 31) / 32 <= kSelThreads) {
+    static_assert(kSelThreads == 1024, "select_key16: one word per thread up to 1024 words");
+    if (select_key16(s.ctx_cap)) {
         if (keys16 != nullptr && sample16 != nullptr)
             return select_t<1, true>(TB_SEL_ARGS);
         return select_t<1, false>(TB_SEL_ARGS);
