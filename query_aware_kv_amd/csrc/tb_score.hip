@@ -29,7 +29,7 @@
 namespace tb {
 namespace {
 
-constexpr int kScoreThreads = 256;
+constexpr int kScoreThreads = 512;
 constexpr int kMaxFusedNew = 8; // appended rows handled inside the score launch
 static_assert(kMaxFusedNew * 32 <= kScoreThreads, "one 16-byte piece of a new row per thread");
 
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
         return;
     }
 
-    // ---- streaming work-group: positions [t0, t0 + 256) below t_new ----
+    // ---- streaming work-group: positions [t0, t0 + kScoreThreads) below t_new ----
     const int t0 = tile * kScoreThreads;
     if (t0 >= t_new)
         return;
