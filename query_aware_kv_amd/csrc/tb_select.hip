@@ -11,19 +11,23 @@
 //      >= n get key 0, below every real key).  Rows of up to 1024 words keep
 //      their keys in registers (read once, in 16-byte loads); longer rows
 //      re-read them (from L2) at each pass.  In the fused step the score
-//      launch has also stored the top 16 bits of every key (and compactly for
-//      positions 8m); rows of up to 1024 words then take steps 2's sample and
-//      first pass from those (half the bytes, the sample first), and read full
-//      keys only for the candidates and the fallback.
+//      launch has also stored the top 16 bits of every key, within each
+//      32-position word in pair order (positions j and j + 16 side by side),
+//      and compactly for positions 8m; rows of up to 1024 words then take
+//      step 2's sample and first pass from those (half the bytes, the sample
+//      requested first), classify two keys per packed 16-bit op, and read
+//      full keys only for the candidates and the fallback.
 //   2. The B-th largest key tau is bracketed from a sample of one position in
 //      eight (positions 8m): the sample goes into a 4096-bin histogram of the
 //      keys' top 12 bits, and two bins a safe margin either side of the
 //      sample quantile B/m (m: positions competing) bound a candidate range.
-//      One compare-only pass marks the keys above it (kept) and in it; the
-//      candidates' (key, position) pairs are compacted per wave into LDS and
-//      counted by their top 20 bits.  When tau provably lies in the range and
-//      the candidates fit, tau is found from that histogram and one over the
-//      low 12 bits of the candidates sharing its top 20 bits.  Otherwise a
+//      One compare-only pass marks the keys above it (kept) and in it; each
+//      wave lists its candidates' positions in LDS, re-reads their keys with
+//      its lanes sharing the reads evenly, and counts them by their top 20
+//      bits.  When tau provably lies in the range and the candidates fit,
+//      that histogram gives tau's top 20 bits; candidates above them are
+//      kept, and the few sharing them are ranked by one wave (a histogram
+//      of their low 12 bits when more than 64 share them).  Otherwise a
 //      radix select runs over every key: from the top, 8 bits per pass, over
 //      the keys that match the prefix found so far, with the histogram in
 //      LDS as 16 copies (lane mod 16) padded so that equal digits in
@@ -39,13 +43,12 @@
 //      local window (the last n_local positions) are always kept; only the
 //      positions between them compete for the budget (their keys are the
 //      only non-zero ones), and both ranges are ORed in after the dilation.
-//   5. A block scan of per-word popcounts gives |S| and, when the list is
-//      asked for, compacts the bitmap into the ascending index list; the
-//      bitmap itself can be written out too.
+//   5. A block count of set bits gives |S|; when the list is asked for, a
+//      block scan of per-word popcounts compacts the bitmap into the
+//      ascending index list.  The bitmap itself can be written out too.
 #include "tb_internal.h"
 
 #include <atomic>
-
 
 namespace tb {
 namespace {
