@@ -4,9 +4,12 @@
 // Significance: the full KV cache stays resident and each decode step reads
 // only the selected tokens; attention over them is ordinary softmax attention.
 //
-// Grid: (position chunk of kAttnChunk tokens, KV head, sequence).  A
-// work-group handles one KV head and one chunk for all the query heads that
-// share it (GQA):
+// Grid: (chunk of kAttnChunk positions, KV head, sequence).  A work-group
+// handles one KV head and one chunk for all the query heads that share it
+// (GQA).  With bitmaps a chunk is every nchunk-th 32-position word of the
+// row, so each work-group takes an equal share of any dense region (an
+// always-kept window, the sink, new tokens); with lists it is a contiguous
+// range, located in the lists by binary search.
 //   1. Each query head is served by 8/GQ of the eight waves, each wave taking
 //      a part of the chunk.  A wave's membership words come, one per lane,
 //      either straight from the head's selection bitmap (one 32-bit word per
@@ -107,12 +110,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int nchunk = gridDim.x;
     const int c0 = c * kAttnChunk;
+    // The work-group's 32 bitmap words: in bitmap mode the words c,
+    // c + nchunk, c + 2 nchunk, ... of the row (so every work-group takes an
+    // equal share of any dense region: an always-kept window, the sink, new
+    // tokens); in list mode the contiguous words of positions
+    // [c0, c0 + kAttnChunk).  A chunk-local position 32 k + j (word k, bit j)
+    // is row position 32 gword(k) + j.
+    auto gword = [&](int k) { return BITMAP ? c + nchunk * k : c * NWD + k; };
+    auto gpos = [&](uint32_t local) {
+        return 32u * (uint32_t)gword((int)(local >> 5)) + (local & 31u);
+    };
     const size_t head0 = (size_t)b * a.Hq + (size_t)g * GQ; // first query head of the group
     const int slot = lane / LPR, sub = lane % LPR;
 
     // Wave w serves query head hw = w / WPH on part wpart = w % WPH of the
-    // chunk: positions [c0 + wpart * PW, c0 + (wpart + 1) * PW), which are
-    // bitmap words wpart * WPW .. + WPW - 1 of the chunk, one per lane.
+    // chunk: chunk-local positions [wpart * PW, (wpart + 1) * PW), which are
+    // the chunk's words wpart * WPW .. + WPW - 1, one per lane.
     const int hw = wave / WPH, wpart = wave % WPH;
     constexpr int WPW = PW / 32;
     static_assert(WPW <= 64 && WPW % 2 == 0, "a part's words fit one wave, in pairs");
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     // q slice of this lane for the wave's head (kept in the storage type;
     // bf16 pairs feed v_dot2) and, in bitmap mode, this lane's word.
     const uint4 qh = *reinterpret_cast<const uint4 *>(q + (head0 + hw) * D + sub * EPL);
-    const int p0w = c0 + 32 * (wpart * WPW + lane); // first position of this lane's word
+    const int p0w = 32 * gword(wpart * WPW + lane); // first position of this lane's word
     uint32_t word = 0u;
     if constexpr (BITMAP) {
         // query head h follows importance head h / (Hq / Himp), a power-of-two
@@ -133,8 +146,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     }
     const int kf_raw = a.keep_from != nullptr ? a.keep_from[b] : a.cap;
     const int n = clamp_len(a.ctx_len[b], a.cap);
-    const int c1 = min(c0 + kAttnChunk, n);
-    const bool active = c0 < n;
+    // positions of the chunk are below c1 (and those of a word below n)
+    const int c1 = BITMAP ? n : min(c0 + kAttnChunk, n);
+    const bool active = BITMAP ? 32 * c < n : c0 < n;
+    const int nact = BITMAP ? min(nchunk, (n + 31) / 32) : (n + kAttnChunk - 1) / kAttnChunk;
 
     if (active) {
         // ---- 1. the wave's membership words ----
@@ -164,7 +179,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 word = bm[hw][wpart * WPW + lane];
         }
         if (lane < WPW) {
-            // clip to [c0, c1) and add the always-kept range [kf, n)
+            // clip to the chunk's positions below c1 and add the always-kept
+            // range [kf, n)
             const int lo = max(kf, p0w), hi = min(c1, p0w + 32);
             if (hi - p0w < 32)
                 word &= hi <= p0w ? 0u : ((1u << (hi - p0w)) - 1u);
@@ -197,14 +213,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
 #pragma unroll
         for (int e = 0; e < EPL; ++e)
             acc[e] = 0.f;
-        const size_t kvbase = ((size_t)b * a.Hkv + g) * a.cap + c0;
+        const size_t kvbase = ((size_t)b * a.Hkv + g) * a.cap;
         const T *kb = kc + kvbase * D + sub * EPL;
         const T *vb = vc + kvbase * D + sub * EPL;
 
         // All of a slot's rows (up to kRowsInFlight) are requested before any
         // is used.  The loads are unconditional -- a missing row reads the
-        // chunk's first row, which always exists, and is given weight 0 -- so
-        // they issue back to back.
+        // chunk's first position, which always exists, and is given weight
+        // 0 -- so they issue back to back.
         for (uint32_t base = slot; base < nh; base += kRowsInFlight * RPW) {
             uint32_t pos[kRowsInFlight];
             bool ok[kRowsInFlight];
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
             for (int r = 0; r < kRowsInFlight; ++r) {
                 const uint32_t u = base + r * RPW;
                 ok[r] = u < nh;
-                pos[r] = ok[r] ? hlist[wave][u] : 0u;
+                pos[r] = gpos(ok[r] ? hlist[wave][u] : 0u);
             }
 #pragma unroll
             for (int r = 0; r < kRowsInFlight; ++r) {
@@ -290,7 +306,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     // ---- 5. arrival; the last work-group of this (b, g) merges the chunks ----
     arrive_and_combine<T, D, GQ, kAttnThreads, kMaxChunks>(
         cmb, &a.counters[(size_t)b * a.Hkv + g], a.part_o, a.part_ml, nchunk,
-        (n + kAttnChunk - 1) / kAttnChunk, head0, (T *)a.out);
+        nact, head0, (T *)a.out);
 }
 
 template <typename T, int D, int GQ>

@@ -107,8 +107,15 @@ def test_stage_parity(w):
         ref = orc.attend(q64[h], K64[_kv(w, h)], V64[_kv(w, h)], A, w.softmax_scale)
         err = max(err, float(np.abs(f64(out[b, h]) - ref).max()))
     assert err <= TOL[w.dtype], err
-    # list and bitmap membership run the same arithmetic in the same order
-    assert torch.equal(out, out2)
+    # list membership (contiguous chunks) and bitmap membership (interleaved
+    # chunks) visit the rows in different chunk orders: the same values up
+    # to rounding, each within the tolerance of the oracle
+    err2 = max(float(np.abs(f64(out2[b, h]) - orc.attend(
+        q64[h], K64[_kv(w, h)], V64[_kv(w, h)],
+        sorted(set(S_ref[_imp(w, h)].tolist()) | {ctx - 1}), w.softmax_scale)).max())
+        for h in range(w.n_q_heads))
+    assert err2 <= TOL[w.dtype], err2
+    assert float((out.float() - out2.float()).abs().max()) <= TOL[w.dtype]
 
 
 # --------------------------------------------------------------------------
@@ -244,8 +251,12 @@ def _small(**kw) -> Workload:
     dict(n_sink=4, n_local=64),                       # sink and local window
     dict(n_sink=800, n_local=1500, budget=20),        # the buffers cover every context
     dict(n_sink=3, n_local=5, radius=2, dtype="f32", head_dim=64, d_imp=16),
+    # one importance head per KV head: a group's query heads share their
+    # rows, which the attention streams once for all of them
+    dict(n_q_heads=16, n_kv_heads=2, n_imp_heads=2),
+    dict(dtype="f32", head_dim=64, d_imp=16, n_imp_heads=2),
 ], ids=["base", "f32", "imp_per_kv", "group8", "B1", "dense", "r40", "mha_d64", "sink_local",
-        "buffers_cover", "sink_local_f32"])
+        "buffers_cover", "sink_local_f32", "group8_shared", "f32_shared"])
 def test_ragged_batch_fused(kw):
     # three sequences of different lengths (1, 700 and 2000 tokens) in one launch
     w = _small(**kw)
