@@ -250,8 +250,8 @@ size_t tb_mlp_workspace_bytes(const tb_mlp_shape *shape);
  * tb_score / tb_decode_step for its consumer layer (batch = M).  No biases.
  * Products are accumulated in fp32 on the matrix cores; round() is to the
  * dtype, nearest even.  h, w1, w2 16-byte aligned; the workspace (at least
- * tb_mlp_workspace_bytes(), 256-byte aligned, zero-filled before first use)
- * holds the hidden layer and split-K partials and is left reusable.
+ * tb_mlp_workspace_bytes(), 256-byte aligned, no initial contents needed)
+ * holds the hidden layer.
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE, TB_EHIP.
  */
 int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1, const void *w2,

@@ -257,14 +257,11 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        hipStream_t st);
 
 // Importance-query producer (tb_mlp.hip).  Workspace layout in bytes.
-constexpr int kMlpKGrain = 256; // k values per k-slice are a multiple of this
+constexpr int kMlpKGrain = 256; // K of both layers is a multiple of this
 struct MlpLayout {
-    size_t hidden;   // [M][F] hidden layer in the dtype
-    size_t part;     // split-K fp32 partials
-    size_t counters; // per 64-column block arrival counters (kept zero)
+    size_t hidden; // [M][F] hidden layer in the dtype
     size_t total;
 };
-int mlp_k_slices(int K, int N);
 MlpLayout mlp_layout(const tb_mlp_shape &s);
 hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, const void *w2,
                       void *q_imp, void *ws, hipStream_t st);

@@ -11,29 +11,30 @@
 // written slot-major: q_imp[g][m][i][j] = q[m][(g * Himp + i) * d + j], so
 // slot g is the [M][Himp][d] importance query that tb_score takes.
 //
-// Each layer is one launch of a split-K GEMM (k-slices are multiples of
-// kMlpKGrain values, so a wave's loop covers whole groups of kMlpUnroll
-// pieces).  Grid: (64-column block of the
-// output, k-slice); 256 threads, wave w owns 16 output columns.  A wave
-// multiplies its k-slice with MFMA 16x16 tiles, one accumulator tile per 16
-// tokens: lane l supplies token / column l % 16 and the l / 16-th quarter of
-// each k group from one 16-byte piece (bf16: one 16x16x32 step per piece;
-// fp32: four 16x16x4 steps per piece).  Token rows past M read as zero.
-// With one k-slice the tile is finished in registers; otherwise the
-// k-slices' fp32 partials go to the workspace (agent-scope stores, which
-// reach the device coherence point) and the last work-group of a column
-// block to arrive sums them in k-slice order -- the result does not depend
-// on arrival order -- applies the activation, rounds to the dtype, writes
-// the output and resets the block's counter to zero.
+// Each layer is one launch: one work-group per 16 output columns, one wave
+// per k-slice (K / 256 slices, at most 16 waves; a wave takes the 256-value
+// chunks w, w + waves, ...).  A wave multiplies its slice with MFMA 16x16
+// tiles, one accumulator tile per 16 tokens: lane l supplies token / column
+// l % 16 and the l / 16-th quarter of each k group from one 16-byte piece
+// (bf16: one 16x16x32 step per piece; fp32: four 16x16x4 steps per piece).
+// Token rows past M read as zero.  The waves' fp32 tiles meet in LDS and
+// are summed in slice order -- no partials leave the work-group, and the
+// result does not depend on timing -- then activated, rounded to the dtype
+// and written.  One token (a decode step) is a matrix-vector product: there
+// each wave takes R weight rows and reads them in whole 1 KB pieces (one
+// 16-byte piece per lane, every load coalesced), the token's matching pieces
+// in registers, an fp32 fma chain per lane in piece order and a wave sum per
+// row.
 #include "tb_internal.h"
 
 namespace tb {
 namespace {
 
-constexpr int kMlpThreads = 256;
-constexpr int kMlpCols = 64;  // output columns per work-group (16 per wave)
-constexpr int kMlpUnroll = 8; // 16-byte pieces per lane requested together
-constexpr int kMlpSumBatch = 8; // k-slice partials loaded together by the finisher
+constexpr int kMlpCols = 16;     // output columns per work-group (one MFMA tile)
+constexpr int kMlpMaxWaves = 16; // k-slices per work-group
+// 16-byte pieces per lane requested together (fewer with more token tiles,
+// whose pieces take more registers)
+template <int MT> constexpr int mlp_unroll() { return MT >= 4 ? 2 : MT >= 3 ? 4 : 8; }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -42,9 +43,7 @@ struct LayerArgs {
     const void *x;      // [M][K]
     const void *w;      // [N][K]
     void *y;            // [M][N], or slot-major [N / slot][M][slot]
-    float *part;        // [KS][M][N] fp32 partials
-    uint32_t *counters; // [N / kMlpCols], zero between calls
-    int M, K, N, KS;
+    int M, K, N;
     int slot;           // columns per slot of a slot-major output (0: row-major)
     int act;            // TB_ACT_RELU / TB_ACT_SILU, or -1 for none
 };
@@ -71,151 +70,182 @@ __device__ __forceinline__ void store_out(const LayerArgs &a, int m, int n, floa
 }
 
 template <typename T, int MT>
-__global__ __launch_bounds__(kMlpThreads) void mlp_layer_kernel(LayerArgs a)
+__global__ __launch_bounds__(64 * kMlpMaxWaves) void mlp_layer_kernel(LayerArgs a)
 {
     constexpr int EPL = 16 / (int)sizeof(T); // k values per lane piece
     constexpr int GK = 4 * EPL;              // k values per piece group (4 lane quarters)
-    static_assert(kMlpKGrain % (GK * kMlpUnroll) == 0, "whole unrolled groups per k-slice");
+    constexpr int UNR = mlp_unroll<MT>();
+    constexpr int CHUNK = GK * UNR;          // k values per wave iteration
+    static_assert(kMlpKGrain % CHUNK == 0, "whole iterations per 256-value chunk");
+    extern __shared__ f32x4 tiles[];         // [waves][MT][64]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nb = blockIdx.x, ks = blockIdx.y;
-    const int n0 = nb * kMlpCols + wave * 16;
-    const int kslice = a.K / a.KS, kbeg = ks * kslice;
+    const int nwaves = (int)blockDim.x / 64;
+    const int n0 = blockIdx.x * kMlpCols;
     const int r = lane & 15, q4 = lane >> 4;
 
-    const T *wrow = (const T *)a.w + (size_t)(n0 + r) * a.K + kbeg + EPL * q4;
+    const T *wrow = (const T *)a.w + (size_t)(n0 + r) * a.K + EPL * q4;
     const T *xrow[MT];
     bool xin[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         xin[t] = 16 * t + r < a.M;
-        xrow[t] = (const T *)a.x + (size_t)(xin[t] ? 16 * t + r : 0) * a.K + kbeg + EPL * q4;
+        xrow[t] = (const T *)a.x + (size_t)(xin[t] ? 16 * t + r : 0) * a.K + EPL * q4;
     }
     f32x4 acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k = 0; k < kslice; k += GK * kMlpUnroll) {
-        uint4 bp[kMlpUnroll], ap[MT][kMlpUnroll];
+    // this wave's slice: 256-value chunks wave, wave + nwaves, ...
+    for (int k0 = wave * kMlpKGrain; k0 < a.K; k0 += nwaves * kMlpKGrain) {
+        for (int k = k0; k < k0 + kMlpKGrain; k += CHUNK) {
+            uint4 bp[UNR], ap[MT][UNR];
 #pragma unroll
-        for (int u = 0; u < kMlpUnroll; ++u)
-            bp[u] = *reinterpret_cast<const uint4 *>(wrow + k + u * GK);
+            for (int u = 0; u < UNR; ++u)
+                bp[u] = *reinterpret_cast<const uint4 *>(wrow + k + u * GK);
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int u = 0; u < kMlpUnroll; ++u)
-                ap[t][u] = *reinterpret_cast<const uint4 *>(xrow[t] + k + u * GK);
+                for (int u = 0; u < UNR; ++u)
+                    ap[t][u] = *reinterpret_cast<const uint4 *>(xrow[t] + k + u * GK);
 #pragma unroll
-        for (int u = 0; u < kMlpUnroll; ++u)
+            for (int u = 0; u < UNR; ++u)
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const uint4 av = xin[t] ? ap[t][u] : make_uint4(0u, 0u, 0u, 0u);
-                if constexpr (sizeof(T) == 2) {
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bp[u]), acc[t],
-                        0, 0, 0);
-                } else {
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        __uint_as_float(av.x), __uint_as_float(bp[u].x), acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        __uint_as_float(av.y), __uint_as_float(bp[u].y), acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        __uint_as_float(av.z), __uint_as_float(bp[u].z), acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        __uint_as_float(av.w), __uint_as_float(bp[u].w), acc[t], 0, 0, 0);
+                for (int t = 0; t < MT; ++t) {
+                    const uint4 av = xin[t] ? ap[t][u] : make_uint4(0u, 0u, 0u, 0u);
+                    if constexpr (sizeof(T) == 2) {
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bp[u]),
+                            acc[t], 0, 0, 0);
+                    } else {
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            __uint_as_float(av.x), __uint_as_float(bp[u].x), acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            __uint_as_float(av.y), __uint_as_float(bp[u].y), acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            __uint_as_float(av.z), __uint_as_float(bp[u].z), acc[t], 0, 0, 0);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            __uint_as_float(av.w), __uint_as_float(bp[u].w), acc[t], 0, 0, 0);
+                    }
                 }
-            }
+        }
     }
 
-    // acc[t][i] is the tile element (token 16t + 4*q4 + i, column n0 + r)
+    // acc[t][i] is the slice's tile element (token 16t + 4*q4 + i, column
+    // n0 + r); the slices are summed in order by wave 0
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+        tiles[(wave * MT + t) * 64 + lane] = acc[t];
+    __syncthreads();
+    if (wave != 0)
+        return;
     const int n = n0 + r;
-    if (a.KS == 1) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 16 * t + 4 * q4 + i;
-                if (m < a.M)
-                    store_out<T>(a, m, n, acc[t][i]);
-            }
-        return;
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t = 0; t < MT; ++t) {
+        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nwaves; ++w)
+            sum += tiles[(w * MT + t) * 64 + lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 16 * t + 4 * q4 + i;
             if (m < a.M)
-                __hip_atomic_store(&a.part[((size_t)ks * a.M + m) * a.N + n], acc[t][i],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                store_out<T>(a, m, n, sum[i]);
         }
-    // The partial stores complete (vmcnt 0) before the counter moves; the
-    // signal fence keeps the compiler from sinking them below it.
-    __shared__ uint32_t last;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&a.counters[nb], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last = old == (uint32_t)(a.KS - 1) ? 1u : 0u;
     }
-    __syncthreads();
-    if (last == 0u)
-        return;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    float sum[MT][4];
+}
+
+// One token: wave v of the work-group owns weight rows R * (4 * blockIdx.x
+// + v) .. + R - 1; NCH = K / (64 * 16 / sizeof(T)) pieces per row.
+constexpr int kGemvWaves = 4;
+template <typename T, int NCH, int R>
+__global__ __launch_bounds__(64 * kGemvWaves) void gemv_kernel(LayerArgs a)
+{
+    constexpr int EPL = 16 / (int)sizeof(T);
+    constexpr int KC = 64 * EPL; // k values per piece (a whole wave)
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row0 = R * (kGemvWaves * blockIdx.x + wave);
+    const T *xb = (const T *)a.x + EPL * lane;
+    const T *wb = (const T *)a.w + (size_t)row0 * a.K + EPL * lane;
+    uint4 xp[NCH], wp[R][NCH];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int c = 0; c < NCH; ++c)
+        xp[c] = *reinterpret_cast<const uint4 *>(xb + c * KC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sum[t][i] = 0.f;
-    // every partial of a batch of k-slices is requested before any is added
-    constexpr int SB = MT == 1 ? kMlpSumBatch : kMlpSumBatch / 2;
-    for (int k0 = 0; k0 < a.KS; k0 += SB) {
-        float v[SB][MT][4];
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int b2 = 0; b2 < SB; ++b2)
+        for (int c = 0; c < NCH; ++c)
+            wp[r][c] = *reinterpret_cast<const uint4 *>(wb + (size_t)r * a.K + c * KC);
+    float acc[R];
 #pragma unroll
-            for (int t = 0; t < MT; ++t)
+    for (int r = 0; r < R; ++r) {
+        acc[r] = 0.f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = 16 * t + 4 * q4 + i, k2 = k0 + b2;
-                    v[b2][t][i] =
-                        m < a.M && k2 < a.KS
-                            ? __hip_atomic_load(&a.part[((size_t)k2 * a.M + m) * a.N + n],
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : 0.f;
-                }
+        for (int c = 0; c < NCH; ++c) {
+            T xv[EPL], wv[EPL];
+            __builtin_memcpy(xv, &xp[c], 16);
+            __builtin_memcpy(wv, &wp[r][c], 16);
 #pragma unroll
-        for (int b2 = 0; b2 < SB; ++b2)
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sum[t][i] += v[b2][t][i]; // k-slice order
+            for (int e = 0; e < EPL; ++e)
+                acc[r] = fmaf(to_f32(xv[e]), to_f32(wv[e]), acc[r]);
+        }
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 16 * t + 4 * q4 + i;
-            if (m < a.M)
-                store_out<T>(a, m, n, sum[t][i]);
-        }
-    if (tid == 0)
-        __hip_atomic_store(&a.counters[nb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int r = 0; r < R; ++r) {
+        const float v = wave_sum(acc[r]);
+        if (lane == r)
+            store_out<T>(a, 0, row0 + r, v);
+    }
+}
+
+template <typename T, int NCH>
+hipError_t gemv_r(const LayerArgs &a, hipStream_t st)
+{
+    // about 256 work-groups: R rows per wave
+    const int R = a.N >= 4 * 1024 ? 4 : a.N >= 2 * 1024 ? 2 : 1;
+    const dim3 grid(a.N / (kGemvWaves * R)), block(64 * kGemvWaves);
+    if (R == 4)
+        hipLaunchKernelGGL((gemv_kernel<T, NCH, 4>), grid, block, 0, st, a);
+    else if (R == 2)
+        hipLaunchKernelGGL((gemv_kernel<T, NCH, 2>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((gemv_kernel<T, NCH, 1>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+// The one-token path, when K is a power-of-two number of whole pieces (at
+// most 16); otherwise hipErrorNotSupported and the MFMA path runs.
+template <typename T>
+hipError_t gemv_t(const LayerArgs &a, hipStream_t st)
+{
+    constexpr int KC = 64 * 16 / (int)sizeof(T);
+    if (a.M != 1 || a.K % KC != 0 || a.N % (kGemvWaves * 4) != 0)
+        return hipErrorNotSupported;
+    switch (a.K / KC) {
+    case 1: return gemv_r<T, 1>(a, st);
+    case 2: return gemv_r<T, 2>(a, st);
+    case 4: return gemv_r<T, 4>(a, st);
+    case 8: return gemv_r<T, 8>(a, st);
+    case 16: return gemv_r<T, 16>(a, st);
+    }
+    return hipErrorNotSupported;
 }
 
 template <typename T>
 hipError_t layer_t(const LayerArgs &a, hipStream_t st)
 {
-    const dim3 grid(a.N / kMlpCols, a.KS);
-    switch ((a.M + 15) / 16) {
-    case 1: hipLaunchKernelGGL((mlp_layer_kernel<T, 1>), grid, dim3(kMlpThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((mlp_layer_kernel<T, 2>), grid, dim3(kMlpThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((mlp_layer_kernel<T, 3>), grid, dim3(kMlpThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((mlp_layer_kernel<T, 4>), grid, dim3(kMlpThreads), 0, st, a); break;
+    const hipError_t g = gemv_t<T>(a, st);
+    if (g != hipErrorNotSupported)
+        return g;
+    const int chunks = a.K / kMlpKGrain;
+    const int waves = chunks < kMlpMaxWaves ? chunks : kMlpMaxWaves;
+    const dim3 grid(a.N / kMlpCols);
+    const int mt = (a.M + 15) / 16;
+    const size_t lds = (size_t)waves * mt * 64 * sizeof(f32x4);
+    switch (mt) {
+    case 1: hipLaunchKernelGGL((mlp_layer_kernel<T, 1>), grid, dim3(64 * waves), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((mlp_layer_kernel<T, 2>), grid, dim3(64 * waves), lds, st, a); break;
+    case 3: hipLaunchKernelGGL((mlp_layer_kernel<T, 3>), grid, dim3(64 * waves), lds, st, a); break;
+    case 4: hipLaunchKernelGGL((mlp_layer_kernel<T, 4>), grid, dim3(64 * waves), lds, st, a); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -228,32 +258,12 @@ hipError_t layer(const tb_mlp_shape &s, const LayerArgs &a, hipStream_t st)
 
 } // namespace
 
-int mlp_k_slices(int K, int N)
-{
-    // enough work-groups to cover the chip twice, each k-slice a whole number
-    // of kMlpKGrain values
-    int ks = 1;
-    while ((N / kMlpCols) * ks < 512 && K % (2 * ks * kMlpKGrain) == 0)
-        ks *= 2;
-    return ks;
-}
-
 MlpLayout mlp_layout(const tb_mlp_shape &s)
 {
     MlpLayout L;
-    const int N = s.n_slots * s.n_imp_heads * s.d_imp;
     const size_t elt = s.dtype == TB_BF16 ? 2 : 4;
-    const int ks1 = mlp_k_slices(s.hidden, s.inner), ks2 = mlp_k_slices(s.inner, N);
-    const size_t wide = (size_t)(s.inner > N ? s.inner : N);
-    const size_t kmax = (size_t)(ks1 > ks2 ? ks1 : ks2);
-    size_t off = 0;
-    L.hidden = off;
-    off += align_up((size_t)s.tokens * s.inner * elt);
-    L.part = off;
-    off += align_up(kmax * s.tokens * wide * sizeof(float));
-    L.counters = off;
-    off += align_up(wide / kMlpCols * sizeof(uint32_t));
-    L.total = off;
+    L.hidden = 0;
+    L.total = align_up((size_t)s.tokens * s.inner * elt);
     return L;
 }
 
@@ -267,12 +277,9 @@ hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, cons
     a.x = h;
     a.w = w1;
     a.y = base + L.hidden;
-    a.part = (float *)(base + L.part);
-    a.counters = (uint32_t *)(base + L.counters);
     a.M = s.tokens;
     a.K = s.hidden;
     a.N = s.inner;
-    a.KS = mlp_k_slices(s.hidden, s.inner);
     a.slot = 0;
     a.act = s.act;
     hipError_t e = layer(s, a, st);
@@ -283,7 +290,6 @@ hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, cons
     a.y = q_imp;
     a.K = s.inner;
     a.N = N;
-    a.KS = mlp_k_slices(s.inner, N);
     a.slot = s.n_imp_heads * s.d_imp;
     a.act = -1;
     return layer(s, a, st);
