@@ -211,13 +211,6 @@ struct BinScan {
         return BinHit{64u * L + (uint32_t)x, (uint32_t)__builtin_amdgcn_readlane(up, x),
                       (uint32_t)__builtin_amdgcn_readlane(c, x)};
     }
-    __device__ void clear(uint32_t *hist, int lane_) const
-    {
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-            reinterpret_cast<uint4 *>(hist)[lane_ * 16 + ((c + lane_) & 15)] =
-                make_uint4(0u, 0u, 0u, 0u);
-    }
 };
 
 // Packed unsigned 16-bit saturating subtract and minimum (two keys per op).
