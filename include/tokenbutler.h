@@ -193,8 +193,10 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
  * accumulated in fp32 and rounded to the dtype.  An empty A gives a zero row.
  * sel_idx lists must be ascending and duplicate-free; sel_count is clamped to
  * sel_stride.  When sel_bits is not NULL the selected set is read from that
- * bitmap instead and sel_idx / sel_count are ignored (they may be NULL).
- * Rows shared by several query heads of one KV head are read once.
+ * bitmap instead and sel_idx / sel_count are ignored (they may be NULL);
+ * the two routes accumulate the rows in different orders and agree to
+ * rounding.  Rows that several query heads of one KV head select are
+ * requested at about the same time, so HBM serves each about once.
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
  */
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
