@@ -20,9 +20,12 @@
 //   2. Two consecutive words are the 64-bit mask of 64 positions, so the
 //      wave compacts its positions from scalar masks with no ballot and no
 //      work-group barrier.  Rows that several query heads of the group
-//      select are requested by sibling waves of the same work-group at about
-//      the same time, so the repeats are served from cache and HBM sees each
-//      row about once.
+//      select are requested by sibling waves of the same work-group, and the
+//      repeats are served from L2 as long as the siblings stay close.  With
+//      one work-group per compute unit they do.  With several per unit each
+//      head's waves run at their own pace and drift apart, so there (bitmaps,
+//      16-bit rows of 128) the waves walk their parts in steps of 128
+//      positions with a work-group barrier after each step.
 //   3. Rows stream through the lanes in 16-byte pieces (D*elt/16 lanes per
 //      row, several rows per wave, four rows in flight per row slot); each row
 //      slot keeps an online softmax (running max, sum, fp32 accumulator) for
@@ -37,6 +40,8 @@
 //      weighted sums with all of its threads -- writes the output rows, and
 //      resets the counter to zero for the next call.
 #include "tb_attn_common.h"
+
+#include <atomic>
 
 namespace tb {
 namespace {
@@ -84,8 +89,17 @@ struct AttnArgs {
     void *out;
 };
 
-template <typename T, int D, int GQ, bool BITMAP>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
+// The windowed walk is built where it keeps eight waves per SIMD (four
+// work-groups per compute unit) without spills: 16-bit storage, head_dim 128
+// and at least two query heads per KV head (a lone head shares no rows).
+template <typename T, int D, int GQ> constexpr bool attn_windowed_ok()
+{
+    return sizeof(T) == 2 && D == 128 && GQ >= 2;
+}
+
+template <typename T, int D, int GQ, bool BITMAP, int WIN>
+__global__ __launch_bounds__(kAttnThreads)
+__attribute__((amdgpu_waves_per_eu(WIN > 0 ? 8 : 1))) void attn_kernel(AttnArgs a)
 {
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
@@ -129,6 +143,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
     const int hw = wave / WPH, wpart = wave % WPH;
     constexpr int WPW = PW / 32;
     static_assert(WPW <= 64 && WPW % 2 == 0, "a part's words fit one wave, in pairs");
+    // Windowed walk (WIN > 0, bitmap mode): the waves cover their parts in
+    // steps of WIN word pairs and meet at a barrier after each step, so all
+    // query heads of the group read a shared row within a short time of
+    // each other and the later reads find it in L2.  wend holds the end of
+    // each step in the wave's position list.
+    static_assert(WIN == 0 || (BITMAP && (WPW / 2) % WIN == 0), "whole steps per part");
+    constexpr int NWIN = WIN > 0 ? WPW / 2 / WIN : 1;
+    __shared__ uint16_t wend[kAttnWaves][NWIN];
     // Everything that does not depend on the lengths is requested first: the
     // q slice of this lane for the wave's head (kept in the storage type;
     // bf16 pairs feed v_dot2) and, in bitmap mode, this lane's word.
@@ -203,6 +225,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
                 hlist[wave][nh + __builtin_amdgcn_mbcnt_hi(m_hi, __builtin_amdgcn_mbcnt_lo(m_lo, 0u))] =
                     (uint16_t)(wpart * PW + 64 * k + lane);
             nh += (uint32_t)__popcll(msk);
+            if constexpr (WIN > 0)
+                if (k % WIN == WIN - 1 && lane == 0)
+                    wend[wave][k / WIN] = (uint16_t)nh;
         }
         // the list is written and read by this wave only
         __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0)
@@ -221,43 +246,52 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         // is used.  The loads are unconditional -- a missing row reads the
         // chunk's first position, which always exists, and is given weight
         // 0 -- so they issue back to back.
-        for (uint32_t base = slot; base < nh; base += kRowsInFlight * RPW) {
-            uint32_t pos[kRowsInFlight];
-            bool ok[kRowsInFlight];
-            uint4 kk[kRowsInFlight], vv[kRowsInFlight];
+        uint32_t lo = 0u;
+#pragma unroll 1
+        for (int wi = 0; wi < NWIN; ++wi) {
+            const uint32_t hi =
+                WIN > 0 ? __builtin_amdgcn_readfirstlane((uint32_t)wend[wave][wi]) : nh;
+            for (uint32_t base = lo + slot; base < hi; base += kRowsInFlight * RPW) {
+                uint32_t pos[kRowsInFlight];
+                bool ok[kRowsInFlight];
+                uint4 kk[kRowsInFlight], vv[kRowsInFlight];
 #pragma unroll
-            for (int r = 0; r < kRowsInFlight; ++r) {
-                const uint32_t u = base + r * RPW;
-                ok[r] = u < nh;
-                pos[r] = gpos(ok[r] ? hlist[wave][u] : 0u);
-            }
+                for (int r = 0; r < kRowsInFlight; ++r) {
+                    const uint32_t u = base + r * RPW;
+                    ok[r] = u < hi;
+                    pos[r] = gpos(ok[r] ? hlist[wave][u] : 0u);
+                }
 #pragma unroll
-            for (int r = 0; r < kRowsInFlight; ++r) {
-                kk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pos[r] * D);
-                vv[r] = *reinterpret_cast<const uint4 *>(vb + (size_t)pos[r] * D);
-            }
+                for (int r = 0; r < kRowsInFlight; ++r) {
+                    kk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pos[r] * D);
+                    vv[r] = *reinterpret_cast<const uint4 *>(vb + (size_t)pos[r] * D);
+                }
 #pragma unroll
-            for (int r = 0; r < kRowsInFlight; ++r) {
-                // logit in base 2, reduced over the row's lanes
-                const float z = group_sum<LPR>(lane_dot<T>(qh, kk[r])) * a.qscale;
-                if (ok[r]) {
-                    if (z > m) {
-                        const float corr = __builtin_amdgcn_exp2f(m - z);
-                        l *= corr;
+                for (int r = 0; r < kRowsInFlight; ++r) {
+                    // logit in base 2, reduced over the row's lanes
+                    const float z = group_sum<LPR>(lane_dot<T>(qh, kk[r])) * a.qscale;
+                    if (ok[r]) {
+                        if (z > m) {
+                            const float corr = __builtin_amdgcn_exp2f(m - z);
+                            l *= corr;
+#pragma unroll
+                            for (int e = 0; e < EPL; ++e)
+                                acc[e] *= corr;
+                            m = z;
+                        }
+                        const float pr = __builtin_amdgcn_exp2f(z - m);
+                        l += pr;
+                        T vt[EPL];
+                        __builtin_memcpy(vt, &vv[r], 16);
 #pragma unroll
                         for (int e = 0; e < EPL; ++e)
-                            acc[e] *= corr;
-                        m = z;
+                            acc[e] = fmaf(pr, to_f32(vt[e]), acc[e]);
                     }
-                    const float pr = __builtin_amdgcn_exp2f(z - m);
-                    l += pr;
-                    T vt[EPL];
-                    __builtin_memcpy(vt, &vv[r], 16);
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e)
-                        acc[e] = fmaf(pr, to_f32(vt[e]), acc[e]);
                 }
             }
+            if constexpr (WIN > 0)
+                __syncthreads();
+            lo = hi;
         }
 
         // ---- 4. merge each head's row slots into the chunk partial ----
@@ -309,14 +343,57 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a)
         nact, head0, (T *)a.out);
 }
 
+// Word pairs per step of the windowed walk.
+constexpr int kAttnWindowPairs = 2;
+
+
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int &cus)
+{
+    static std::atomic<int> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    cus = dev < 64 ? known[dev].load(std::memory_order_relaxed) : 0;
+    if (cus > 0)
+        return hipSuccess;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 64)
+        known[dev].store(cus, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
 template <typename T, int D, int GQ>
 hipError_t attn_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
     dim3 grid(attn_chunks(s.ctx_cap), s.n_kv_heads, s.batch);
-    if (a.sel_bits != nullptr)
-        hipLaunchKernelGGL((attn_kernel<T, D, GQ, true>), grid, dim3(kAttnThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((attn_kernel<T, D, GQ, false>), grid, dim3(kAttnThreads), 0, st, a);
+    if (a.sel_bits != nullptr) {
+        // With two or more work-groups per compute unit the others fill the
+        // SIMDs while one waits at a window barrier, and the group's query
+        // heads then share their rows through L2 instead of re-reading them
+        // from HBM.  With one work-group per unit the waits would idle it.
+        int cus = 0;
+        const hipError_t e = device_cus(cus);
+        if (e != hipSuccess)
+            return e;
+        const long wgs = (long)grid.x * grid.y * grid.z;
+        bool windowed = false;
+        if constexpr (attn_windowed_ok<T, D, GQ>())
+            windowed = wgs >= 2L * cus;
+        if constexpr (attn_windowed_ok<T, D, GQ>())
+            if (windowed)
+                hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, kAttnWindowPairs>), grid,
+                                   dim3(kAttnThreads), 0, st, a);
+        if (!windowed)
+            hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, 0>), grid, dim3(kAttnThreads), 0,
+                               st, a);
+    } else {
+        hipLaunchKernelGGL((attn_kernel<T, D, GQ, false, 0>), grid, dim3(kAttnThreads), 0, st,
+                           a);
+    }
     return hipGetLastError();
 }
 

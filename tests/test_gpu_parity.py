@@ -289,6 +289,45 @@ def test_ragged_batch_fused(kw):
                 assert np.abs(f64(out[b, h]) - dense).max() <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("kw", [
+    # 8 query heads per KV head sharing 2 importance heads, sink and window
+    dict(batch=40, n_q_heads=16, n_kv_heads=2, n_imp_heads=4, n_sink=4, n_local=64),
+    # 2 query heads per KV head, one importance head each
+    dict(batch=20, n_q_heads=8, n_kv_heads=4, n_imp_heads=8),
+], ids=["group8", "group2"])
+def test_windowed_attention_walk(kw):
+    # a grid of at least two work-groups per compute unit: the bitmap
+    # attention walks its rows in barrier-separated windows; ragged lengths
+    # leave some chunks with no positions and others ending mid-word
+    w = _small(ctx0=7000, budget=300, **kw)
+    wgs = -(-w.ctx_cap // 1024) * w.n_kv_heads * w.batch
+    assert wgs >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    lens = [w.ctx_cap] * w.batch
+    lens[:4] = [1, 33, 1025, 5000]
+    ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    args = tbl.step_args(dc.shape, dc.params, q=inp.q.cuda(), q_imp=inp.q_imp.cuda(),
+                         k_new=inp.k_new.cuda(), v_new=inp.v_new.cuda(), refresh=True, w=dc.W,
+                         k_cache=dc.K, v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
+                         softmax_scale=w.softmax_scale, sel_idx=None, sel_count=dc.cnt,
+                         sel_bits=dc.bits, keep_from=dc.keep, out=out)
+    tbl.decode_step(dc.shape, dc.params, args, dc.ws)
+    torch.cuda.synchronize()
+    for b in (0, 1, 2, 3, w.batch - 1):
+        n = lens[b]
+        st = oracle_state(w, dc.pre, b)
+        ref = orc.decode_step(st, f64(dc.pre.W), f64(inp.q[b]), f64(inp.q_imp[b]), n, odtype(w),
+                              True, w.softmax_scale, k_new=f64(inp.k_new[b]),
+                              v_new=f64(inp.v_new[b]))
+        got = bitmap_positions(dc.bits, b, n)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        err = float(np.abs(f64(out[b]) - ref).max())
+        assert err <= TOL[w.dtype], (b, err)
+
+
 def _select_case(scores_rows, lens, B, r, n_sink=0, n_local=0):
     """tb_select on crafted fp32 scores [b][H][cap]."""
     bsz, H, cap = scores_rows.shape
