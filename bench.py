@@ -277,6 +277,61 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_dense = e0.elapsed_time(e1) / a.steps
 
+    # prediction interval: a reuse step appends and projects the new token and
+    # attends over the selection the last refresh left in its replica (no
+    # scores, no selection); the mean step over an interval of P steps is one
+    # refresh and P - 1 reuses
+    P = 8
+    reuse_args = [tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=False,
+                                w=W, k_cache=r["K"], v_cache=r["V"], kp_cache=r["Kp"],
+                                ctx_len=ctx, softmax_scale=w.softmax_scale, sel_idx=None,
+                                sel_count=r["cnt"], sel_bits=r["bits"], keep_from=r["keep"],
+                                out=out)
+                  for r in reps]
+    for s in range(a.warmup):
+        tbl.decode_step(shape, params, reuse_args[s % R], ws)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(a.steps):
+        tbl.decode_step(shape, params, reuse_args[s % R], ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_reuse = e0.elapsed_time(e1) / a.steps
+
+    # A reuse step's GPU work is shorter than the time the host needs to issue
+    # a step from Python, so the interval is also timed as HIP-graph replays
+    # (one captured step per replica) of refresh and of reuse steps; each
+    # replay must reproduce the eager output.
+    def graph_ms(args_list):
+        tbl.decode_step(shape, params, args_list[R - 1], ws)
+        torch.cuda.synchronize()
+        ref = out.clone()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for r in range(R):
+                tbl.decode_step(shape, params, args_list[r], ws)
+        for _ in range(2):
+            out.zero_()
+            torch.cuda.synchronize()
+            gr.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref):
+                raise RuntimeError("graph replay of the decode step differs from the eager step")
+        n_rep = max(1, a.steps // R)
+        e0.record(stream)
+        for _ in range(n_rep):
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_rep * R)
+
+    ms_refresh_g = graph_ms(step_args)
+    ms_reuse_g = graph_ms(reuse_args)
+    ms_interval = (ms_refresh_g + (P - 1) * ms_reuse_g) / P
+    log(f"bench: reuse step {ms_reuse * 1e3:.2f} us issued from Python; graph replay: refresh "
+        f"{ms_refresh_g * 1e3:.2f} us, reuse {ms_reuse_g * 1e3:.2f} us; interval of {P}: mean "
+        f"step {ms_interval * 1e3:.2f} us, {ms_dense / ms_interval:.2f}x dense attention")
+
     # the importance-query producer MLP at the step's batch: Llama-3-8B hidden
     # size, inner width 1024, four consumer slots of this shape's heads
     mshape = tbl.make_mlp_shape(w.batch, 4096, 1024, 4, w.n_imp_heads, w.d_imp, q.dtype,
@@ -375,6 +430,12 @@ def main() -> int:
                             "algorithmic_bytes": dense_bytes, "achieved": dense_gbs,
                             "frac": dense_gbs / PEAK_HBM_GBS,
                             "speedup_of_sparse_step": ms_dense / ms_step},
+        "prediction_interval": {"interval": P, "timing": "HIP-graph replay",
+                                "refresh_step_us": ms_refresh_g * 1e3,
+                                "reuse_step_us": ms_reuse_g * 1e3,
+                                "reuse_step_us_issued_from_python": ms_reuse * 1e3,
+                                "mean_step_us": ms_interval * 1e3,
+                                "speedup_vs_dense_attention": ms_dense / ms_interval},
         "predictor_mlp": {"kernel": "two layer launches (tb_predict_queries), HIP-graph replay",
                           "shape": {"tokens": w.batch, "hidden": 4096, "inner": 1024,
                                     "slots": 4, "imp_heads": w.n_imp_heads, "d_imp": w.d_imp},

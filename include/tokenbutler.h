@@ -300,6 +300,9 @@ typedef struct tb_step_args {
  * On a non-refresh step the state (sel_bits and keep_from) is read, not
  * written.  ctx_len[b] - n_new
  * must be >= 0.  Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE.
+ * Launches on `stream`: a refresh step is three (scores, selection,
+ * attention) and a non-refresh step one (attention); up to 8 new rows are
+ * appended inside the first of them, more in a launch of their own before.
  */
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                    const tb_step_args *args, void *ws, size_t ws_bytes, void *stream);

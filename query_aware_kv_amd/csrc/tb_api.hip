@@ -296,9 +296,9 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     hipStream_t st = (hipStream_t)stream;
     const int32_t stride = sel_capacity(*shape, *params);
 
-    // Refresh steps append inside the score launch when there are few new
-    // rows; otherwise (and on reuse steps) a separate launch appends them.
-    const bool fused_append = a->refresh && a->n_new > 0 && a->n_new <= score_max_fused_new();
+    // A few new rows are appended inside the score launch (refresh steps) or
+    // the attention launch (reuse steps); more take a launch of their own.
+    const bool fused_append = a->n_new > 0 && a->n_new <= score_max_fused_new();
     if (a->n_new > 0 && !fused_append)
         TB_TRY(hip_rc(launch_append_project(*shape, a->k_new, a->v_new, a->n_new, a->w,
                                             a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
@@ -314,9 +314,20 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                                     a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
                                     k16 ? W.keys16 : nullptr, k16 ? W.sample16 : nullptr, st)));
     }
+    AttnAppend app;
+    if (!a->refresh && fused_append) {
+        app.k_new = a->k_new;
+        app.v_new = a->v_new;
+        app.w = a->w;
+        app.k_cache = a->k_cache;
+        app.v_cache = a->v_cache;
+        app.kp_cache = a->kp_cache;
+        app.n_new = a->n_new;
+    }
     return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
                               a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,
-                              a->softmax_scale, a->out, W.part_o, W.part_ml, W.counters, st));
+                              a->softmax_scale, a->out, W.part_o, W.part_ml, W.counters, st,
+                              app));
 }
 
 } // extern "C"

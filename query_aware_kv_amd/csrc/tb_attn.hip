@@ -39,6 +39,10 @@
 //      counter) merges the chunk partials -- max and weights first, then the
 //      weighted sums with all of its threads -- writes the output rows, and
 //      resets the counter to zero for the next call.
+// Reuse steps of the fused step append their few new rows inside this
+// launch: one more work-group per (sequence, KV head), dispatched after all
+// attention work-groups, stores them in the caches and projects their keys,
+// while the attention work-groups read those positions from k_new / v_new.
 #include "tb_attn_common.h"
 
 #include <atomic>
@@ -87,7 +91,59 @@ struct AttnArgs {
     float *part_ml;    // [b*Hq][nchunk][2]
     uint32_t *counters;
     void *out;
+    // rows appended by this launch (reuse steps): copied and projected by
+    // one extra work-group per (sequence, KV head), read from k_new / v_new
+    const void *k_new, *v_new, *w;
+    void *k_store, *v_store, *kp;
+    int n_new, d_imp;
+    int nchunk, batch; // chunks per row and sequences (the 1-D grid of an appending launch)
 };
+
+constexpr int kAttnMaxAppend = 8; // rows an attention launch appends
+constexpr int kAttnMaxDImp = 32;
+
+// LDS of the append work-group: W and the new key rows, in the storage type.
+template <typename T, int D> struct AppendLds {
+    T w[D * kAttnMaxDImp];
+    T k[kAttnMaxAppend][D];
+};
+
+// The extra work-group of a (sequence b, KV head g): stores the new rows in
+// the caches and their projected keys (fp64 fma over head_dim in ascending
+// order, rounded once to the storage type, as every projection path does).
+// W and the key rows are staged in LDS first, so each output's serial fma
+// chain reads its operands there.  The attention work-groups of the same
+// launch read these rows from k_new / v_new, never from the cache rows being
+// written.
+template <typename T, int D>
+__device__ void append_rows(const AttnArgs &a, int b, int g, AppendLds<T, D> &S)
+{
+    const int n = clamp_len(a.ctx_len[b], a.cap);
+    const int nfresh = a.n_new < n ? a.n_new : n; // appended rows present in [0, n)
+    const size_t src0 = ((size_t)b * a.Hkv + g) * a.n_new + (a.n_new - nfresh);
+    const size_t dst0 = ((size_t)b * a.Hkv + g) * a.cap + (n - nfresh);
+    constexpr int RP = D * (int)sizeof(T) / 16; // 16-byte pieces per row
+    const int wp = D * a.d_imp * (int)sizeof(T) / 16;
+    for (int e = threadIdx.x; e < wp; e += kAttnThreads)
+        reinterpret_cast<uint4 *>(S.w)[e] = reinterpret_cast<const uint4 *>(a.w)[e];
+    for (int e = threadIdx.x; e < nfresh * RP; e += kAttnThreads) {
+        const int r = e / RP, p = e % RP;
+        const uint4 kv = reinterpret_cast<const uint4 *>((const T *)a.k_new + (src0 + r) * D)[p];
+        const uint4 vv = reinterpret_cast<const uint4 *>((const T *)a.v_new + (src0 + r) * D)[p];
+        reinterpret_cast<uint4 *>((T *)a.k_store + (dst0 + r) * D)[p] = kv;
+        reinterpret_cast<uint4 *>((T *)a.v_store + (dst0 + r) * D)[p] = vv;
+        reinterpret_cast<uint4 *>(S.k[r])[p] = kv;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nfresh * a.d_imp; e += kAttnThreads) {
+        const int r = e / a.d_imp, j = e % a.d_imp;
+        double acc = 0.0;
+#pragma unroll 16
+        for (int i = 0; i < D; ++i)
+            acc = fma(to_f64(S.k[r][i]), to_f64(S.w[i * a.d_imp + j]), acc);
+        ((T *)a.kp)[(dst0 + r) * a.d_imp + j] = from_f64<T>(acc);
+    }
+}
 
 // The windowed walk is built where it keeps eight waves per SIMD (four
 // work-groups per compute unit) without spills: 16-bit storage, head_dim 128
@@ -97,9 +153,9 @@ template <typename T, int D, int GQ> constexpr bool attn_windowed_ok()
     return sizeof(T) == 2 && D == 128 && GQ >= 2;
 }
 
-template <typename T, int D, int GQ, bool BITMAP, int WIN>
+template <typename T, int D, int GQ, bool BITMAP, int WIN, bool APPEND>
 __global__ __launch_bounds__(kAttnThreads)
-__attribute__((amdgpu_waves_per_eu(WIN > 0 ? 8 : 1))) void attn_kernel(AttnArgs a)
+__attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kernel(AttnArgs a)
 {
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
@@ -115,14 +171,39 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 ? 8 : 1))) void attn_kernel(AttnArgs 
     __shared__ float mrg_m[GQ][WPH];
     __shared__ float mrg_l[GQ][WPH];
     __shared__ float mrg_acc[GQ][WPH][D];
-    __shared__ CombineLds<GQ, kAttnThreads> cmb;
+    // the append work-group uses the merge's LDS, which it never reaches
+    __shared__ union {
+        CombineLds<GQ, kAttnThreads> c;
+        AppendLds<T, D> app;
+    } shu;
+    CombineLds<GQ, kAttnThreads> &cmb = shu.c;
 
     const T *__restrict__ q = (const T *)a.q;
     const T *__restrict__ kc = (const T *)a.k;
     const T *__restrict__ vc = (const T *)a.v;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int nchunk = gridDim.x;
+    static_assert(!APPEND || BITMAP, "appending launches read bitmaps");
+    // An appending launch has a 1-D grid: the attention work-groups in
+    // (chunk, KV head, sequence) order, then one append work-group per
+    // (sequence, KV head), dispatched last so that they land beside the
+    // attention work-groups instead of displacing them.
+    int c, g, b, nchunk;
+    if constexpr (APPEND) {
+        nchunk = a.nchunk;
+        const int id = blockIdx.x, nattn = nchunk * a.Hkv * a.batch;
+        if (id >= nattn) {
+            append_rows<T, D>(a, (id - nattn) / a.Hkv, (id - nattn) % a.Hkv, shu.app);
+            return;
+        }
+        c = id % nchunk;
+        g = (id / nchunk) % a.Hkv;
+        b = id / (nchunk * a.Hkv);
+    } else {
+        c = blockIdx.x;
+        g = blockIdx.y;
+        b = blockIdx.z;
+        nchunk = gridDim.x;
+    }
     const int c0 = c * kAttnChunk;
     // The work-group's 32 bitmap words: in bitmap mode the words c,
     // c + nchunk, c + 2 nchunk, ... of the row (so every work-group takes an
@@ -241,6 +322,16 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 ? 8 : 1))) void attn_kernel(AttnArgs 
         const size_t kvbase = ((size_t)b * a.Hkv + g) * a.cap;
         const T *kb = kc + kvbase * D + sub * EPL;
         const T *vb = vc + kvbase * D + sub * EPL;
+        // appending launch: rows from t_new on come from k_new / v_new
+        int t_new = 0;
+        const T *knb = nullptr, *vnb = nullptr;
+        if constexpr (APPEND) {
+            const int nfresh = a.n_new < n ? a.n_new : n;
+            t_new = n - nfresh;
+            const size_t src0 = ((size_t)b * a.Hkv + g) * a.n_new + (a.n_new - nfresh);
+            knb = (const T *)a.k_new + src0 * D + sub * EPL;
+            vnb = (const T *)a.v_new + src0 * D + sub * EPL;
+        }
 
         // All of a slot's rows (up to kRowsInFlight) are requested before any
         // is used.  The loads are unconditional -- a missing row reads the
@@ -263,8 +354,14 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 ? 8 : 1))) void attn_kernel(AttnArgs 
                 }
 #pragma unroll
                 for (int r = 0; r < kRowsInFlight; ++r) {
-                    kk[r] = *reinterpret_cast<const uint4 *>(kb + (size_t)pos[r] * D);
-                    vv[r] = *reinterpret_cast<const uint4 *>(vb + (size_t)pos[r] * D);
+                    const T *kr = kb + (size_t)pos[r] * D, *vr = vb + (size_t)pos[r] * D;
+                    if constexpr (APPEND)
+                        if (pos[r] >= (uint32_t)t_new) {
+                            kr = knb + (size_t)(pos[r] - t_new) * D;
+                            vr = vnb + (size_t)(pos[r] - t_new) * D;
+                        }
+                    kk[r] = *reinterpret_cast<const uint4 *>(kr);
+                    vv[r] = *reinterpret_cast<const uint4 *>(vr);
                 }
 #pragma unroll
                 for (int r = 0; r < kRowsInFlight; ++r) {
@@ -366,34 +463,43 @@ hipError_t device_cus(int &cus)
     return hipSuccess;
 }
 
+template <typename T, int D, int GQ, bool APPEND>
+hipError_t attn_bitmap_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
+{
+    const int nchunk = attn_chunks(s.ctx_cap);
+    const dim3 grid = APPEND ? dim3((nchunk + 1) * s.n_kv_heads * s.batch)
+                             : dim3(nchunk, s.n_kv_heads, s.batch);
+    // With two or more work-groups per compute unit the others fill the
+    // SIMDs while one waits at a window barrier, and the group's query heads
+    // then share their rows through L2 instead of re-reading them from HBM.
+    // With one work-group per unit the waits would idle it.
+    int cus = 0;
+    const hipError_t e = device_cus(cus);
+    if (e != hipSuccess)
+        return e;
+    const long wgs = (long)attn_chunks(s.ctx_cap) * s.n_kv_heads * s.batch;
+    bool windowed = false;
+    if constexpr (attn_windowed_ok<T, D, GQ>())
+        windowed = wgs >= 2L * cus;
+    if constexpr (attn_windowed_ok<T, D, GQ>())
+        if (windowed)
+            hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, kAttnWindowPairs, APPEND>), grid,
+                               dim3(kAttnThreads), 0, st, a);
+    if (!windowed)
+        hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, 0, APPEND>), grid, dim3(kAttnThreads), 0,
+                           st, a);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int GQ>
 hipError_t attn_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
-    dim3 grid(attn_chunks(s.ctx_cap), s.n_kv_heads, s.batch);
-    if (a.sel_bits != nullptr) {
-        // With two or more work-groups per compute unit the others fill the
-        // SIMDs while one waits at a window barrier, and the group's query
-        // heads then share their rows through L2 instead of re-reading them
-        // from HBM.  With one work-group per unit the waits would idle it.
-        int cus = 0;
-        const hipError_t e = device_cus(cus);
-        if (e != hipSuccess)
-            return e;
-        const long wgs = (long)grid.x * grid.y * grid.z;
-        bool windowed = false;
-        if constexpr (attn_windowed_ok<T, D, GQ>())
-            windowed = wgs >= 2L * cus;
-        if constexpr (attn_windowed_ok<T, D, GQ>())
-            if (windowed)
-                hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, kAttnWindowPairs>), grid,
-                                   dim3(kAttnThreads), 0, st, a);
-        if (!windowed)
-            hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, 0>), grid, dim3(kAttnThreads), 0,
-                               st, a);
-    } else {
-        hipLaunchKernelGGL((attn_kernel<T, D, GQ, false, 0>), grid, dim3(kAttnThreads), 0, st,
-                           a);
-    }
+    if (a.sel_bits != nullptr)
+        return a.n_new > 0 ? attn_bitmap_t<T, D, GQ, true>(s, a, st)
+                           : attn_bitmap_t<T, D, GQ, false>(s, a, st);
+    const dim3 grid(attn_chunks(s.ctx_cap), s.n_kv_heads, s.batch);
+    hipLaunchKernelGGL((attn_kernel<T, D, GQ, false, 0, false>), grid, dim3(kAttnThreads), 0, st,
+                       a);
     return hipGetLastError();
 }
 
@@ -416,8 +522,14 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const int32_t *sel_count, const uint32_t *sel_bits,
                        const int32_t *keep_from, const int32_t *ctx_len, float softmax_scale,
                        void *out, float *part_o, float *part_ml, uint32_t *counters,
-                       hipStream_t st)
+                       hipStream_t st, const AttnAppend &app)
 {
+    if (app.n_new > kAttnMaxAppend || s.d_imp > kAttnMaxDImp)
+        return hipErrorInvalidValue;
+    if (app.n_new > 0 && (sel_bits == nullptr || app.k_new == nullptr || app.v_new == nullptr ||
+                          app.w == nullptr || app.k_cache == nullptr ||
+                          app.v_cache == nullptr || app.kp_cache == nullptr))
+        return hipErrorInvalidValue;
     AttnArgs a;
     a.q = q;
     a.k = k_cache;
@@ -441,6 +553,16 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
     a.part_ml = part_ml;
     a.counters = counters;
     a.out = out;
+    a.k_new = app.k_new;
+    a.v_new = app.v_new;
+    a.w = app.w;
+    a.k_store = app.k_cache;
+    a.v_store = app.v_cache;
+    a.kp = app.kp_cache;
+    a.n_new = app.n_new > 0 ? app.n_new : 0;
+    a.d_imp = s.d_imp;
+    a.nchunk = attn_chunks(s.ctx_cap);
+    a.batch = s.batch;
     if (s.dtype == TB_BF16) {
         if (s.head_dim == 64) return attn_gq<bf16_t, 64>(s, a, st);
         if (s.head_dim == 128) return attn_gq<bf16_t, 128>(s, a, st);

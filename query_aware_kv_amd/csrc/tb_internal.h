@@ -249,12 +249,20 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
                          int32_t *keep_from, int n_new, const uint16_t *keys16,
                          const uint16_t *sample16, hipStream_t st);
+// Rows a reuse step appends inside the attention launch (bitmap mode, at
+// most score_max_fused_new() of them): the launch copies them into the
+// caches and projects their keys, and reads them from k_new / v_new.
+struct AttnAppend {
+    const void *k_new = nullptr, *v_new = nullptr, *w = nullptr;
+    void *k_cache = nullptr, *v_cache = nullptr, *kp_cache = nullptr;
+    int n_new = 0;
+};
 hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *sel_idx, int sel_stride,
                        const int32_t *sel_count, const uint32_t *sel_bits,
                        const int32_t *keep_from, const int32_t *ctx_len, float softmax_scale,
                        void *out, float *part_o, float *part_ml, uint32_t *counters,
-                       hipStream_t st);
+                       hipStream_t st, const AttnAppend &app = AttnAppend());
 
 // Importance-query producer (tb_mlp.hip).  Workspace layout in bytes.
 constexpr int kMlpKGrain = 256; // K of both layers is a multiple of this

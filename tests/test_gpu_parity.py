@@ -328,6 +328,45 @@ def test_windowed_attention_walk(kw):
         assert err <= TOL[w.dtype], (b, err)
 
 
+@pytest.mark.parametrize("kw", [dict(steps=4), dict(steps=4, ctx0=7000, budget=300, batch=40,
+                                                   n_q_heads=16, n_kv_heads=2, n_imp_heads=4)],
+                         ids=["small_grid", "windowed_grid"])
+def test_reuse_step_appends_rows(kw):
+    # a refresh step, then a reuse step that appends three rows inside the
+    # attention launch: the cache rows, their projected keys (bit for bit)
+    # and the output follow the oracle
+    w = _small(**kw)
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    rng = np.random.default_rng(77)
+    dt = synth.torch_dtype(w)
+    kn = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv_heads, 3, w.head_dim))).to(dt)
+    vn = torch.from_numpy(rng.standard_normal((w.batch, w.n_kv_heads, 3, w.head_dim))).to(dt)
+    q2 = torch.from_numpy(rng.standard_normal((w.batch, w.n_q_heads, w.head_dim))).to(dt)
+    n = w.ctx0 + 4
+    ctx = torch.full((w.batch,), n, dtype=torch.int32, device="cuda")
+    args = tbl.step_args(dc.shape, dc.params, q=q2.cuda(), q_imp=inp.q_imp.cuda(),
+                         k_new=kn.cuda(), v_new=vn.cuda(), refresh=False, w=dc.W, k_cache=dc.K,
+                         v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
+                         softmax_scale=w.softmax_scale, sel_idx=None, sel_count=dc.cnt,
+                         sel_bits=dc.bits, keep_from=dc.keep, out=out)
+    tbl.decode_step(dc.shape, dc.params, args, dc.ws)
+    torch.cuda.synchronize()
+    for b in (0, 1, w.batch - 1):
+        st = oracle_state(w, dc.pre, b)
+        oracle_step(w, st, dc.pre, inp, 0, b)
+        ref = orc.decode_step(st, f64(dc.pre.W), f64(q2[b]), None, n, odtype(w), False,
+                              w.softmax_scale, k_new=f64(kn[b]), v_new=f64(vn[b]))
+        rows = slice(w.ctx0 + 1, n)
+        assert torch.equal(dc.K[b][:, rows].cpu(), kn[b]) and torch.equal(dc.V[b][:, rows].cpu(), vn[b])
+        np.testing.assert_array_equal(f64(dc.Kp[b][:, rows]), st.Kp[:, rows])
+        assert int(dc.keep[b]) == w.ctx0
+        err = float(np.abs(f64(out[b]) - ref).max())
+        assert err <= TOL[w.dtype], (b, err)
+
+
 def _select_case(scores_rows, lens, B, r, n_sink=0, n_local=0):
     """tb_select on crafted fp32 scores [b][H][cap]."""
     bsz, H, cap = scores_rows.shape
