@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 from query_aware_kv_amd import synth  # noqa: E402
 from query_aware_kv_amd import tokenbutler as tbl  # noqa: E402
-from query_aware_kv_amd.workloads import LLAMA_32K, OFFLOAD_256K  # noqa: E402
+from query_aware_kv_amd.workloads import (BATCHED_8K, INTERVAL_16K, LLAMA_32K,  # noqa: E402
+                                          LONG_128K, OFFLOAD_256K)
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_llama3_8b_ctx32k_traffic.json")
@@ -151,6 +152,85 @@ def offload_leg(steps: int) -> dict:
     return res
 
 
+def workload_leg(w, launches: int) -> dict:
+    """One layer's fused step of another workload, HBM resident: refresh
+    steps (and, with a prediction interval, reuse steps), each timed over
+    `launches` eager launches with HIP events.  Cache replicas (one GB in
+    all) rotate between launches so the 256 MB MALL cannot carry a step's
+    rows over to the next.  Bytes = projected keys of the context + unique
+    gathered K/V rows per KV group (from the library's own bitmaps)."""
+    dev = "cuda:0"
+    pre = synth.prefill(w)
+    inp = synth.step_inputs(w, 0, pre)
+    shape = tbl.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.n_imp_heads, w.head_dim,
+                           w.d_imp, w.ctx_cap, synth.torch_dtype(w))
+    params = tbl.make_params(w.budget, w.radius, w.n_sink, w.n_local)
+    K0, V0, W = pre.K.to(dev), pre.V.to(dev), pre.W.to(dev)
+    Kp0 = torch.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.d_imp), dtype=K0.dtype, device=dev)
+    tbl.project_keys(shape, K0, W, torch.zeros(w.batch, dtype=torch.int32, device=dev), w.ctx0,
+                     Kp0)
+    per = (K0.numel() + V0.numel() + Kp0.numel()) * K0.element_size()
+    R = max(2, -(-(1 << 30) // per))
+    reps = [dict(K=K0.clone(), V=V0.clone(), Kp=Kp0.clone(),
+                 cnt=torch.zeros((w.batch, w.n_imp_heads), dtype=torch.int32, device=dev),
+                 bits=torch.zeros((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)),
+                                  dtype=torch.int32, device=dev),
+                 keep=torch.zeros(w.batch, dtype=torch.int32, device=dev)) for _ in range(R)]
+    del K0, V0, Kp0
+    ws = tbl.alloc_workspace(shape, params, dev)
+    ctx = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
+    q, qi = inp.q.to(dev), inp.q_imp.to(dev)
+    kn, vn = inp.k_new.to(dev), inp.v_new.to(dev)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=q.dtype, device=dev)
+
+    def args(r, refresh):
+        return tbl.step_args(shape, params, q=q, q_imp=qi, k_new=kn, v_new=vn, refresh=refresh,
+                             w=W, k_cache=r["K"], v_cache=r["V"], kp_cache=r["Kp"], ctx_len=ctx,
+                             softmax_scale=w.softmax_scale, sel_idx=None, sel_count=r["cnt"],
+                             sel_bits=r["bits"], keep_from=r["keep"], out=out)
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(arg_list):
+        for i in range(max(R, 10)):
+            tbl.decode_step(shape, params, arg_list[i % R], ws)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(launches):
+            tbl.decode_step(shape, params, arg_list[i % R], ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches
+
+    ms_refresh = timed([args(r, True) for r in reps])
+    uniq = sum(unique_rows(reps[0]["bits"][b:b + 1], w, w.ctx)[0] for b in range(w.batch))
+    row = w.head_dim * w.elt_bytes
+    kp_bytes = w.batch * w.n_kv_heads * w.ctx * w.d_imp * w.elt_bytes
+    by = kp_bytes + uniq * 2 * row
+    res = {"batch": w.batch, "ctx": w.ctx, "budget": w.budget, "radius": w.radius,
+           "interval": w.interval, "replicas": R, "refresh_step_us": ms_refresh * 1e3,
+           "unique_rows": uniq, "unique_row_fraction": uniq / (w.batch * w.n_kv_heads * w.ctx),
+           "algorithmic_bytes": by, "achieved": by / (ms_refresh * 1e-3) / 1e9,
+           "frac": by / (ms_refresh * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    msg = (f"bench: {w.name}: refresh step {ms_refresh * 1e3:.1f} us, {by / 1e6:.0f} MB, "
+           f"{res['achieved']:.0f} GB/s")
+    if w.interval > 1:
+        ms_reuse = timed([args(r, False) for r in reps])
+        by_r = uniq * 2 * row + w.batch * w.n_kv_heads * w.d_imp * w.elt_bytes
+        ms_mean = (ms_refresh + (w.interval - 1) * ms_reuse) / w.interval
+        by_mean = (by + (w.interval - 1) * by_r) / w.interval
+        res.update({"reuse_step_us": ms_reuse * 1e3, "mean_step_us": ms_mean * 1e3,
+                    "mean_achieved": by_mean / (ms_mean * 1e-3) / 1e9,
+                    "mean_frac": by_mean / (ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS})
+        msg += (f"; reuse step {ms_reuse * 1e3:.1f} us; mean over {w.interval}: "
+                f"{ms_mean * 1e3:.1f} us, {res['mean_achieved']:.0f} GB/s")
+    log(msg)
+    del reps, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, pre, inp, seconds: float, max_steps: int) -> dict:
     import oracle as orc
     f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()  # noqa: E731
@@ -187,6 +267,9 @@ def main() -> int:
                     help="most recent tokens always kept (local window)")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the 256K CPU-offloaded K/V leg")
+    ap.add_argument("--other-workloads", action="store_true",
+                    help="also time one layer of the batch-16 8K, batch-4 16K interval and "
+                         "128K workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter scaling)")
     a = ap.parse_args()
@@ -395,6 +478,10 @@ def main() -> int:
 
     offload = None if a.no_offload else offload_leg(max(4, min(a.steps, 20)))
 
+    others = None
+    if a.other_workloads:
+        others = {wl.name: workload_leg(wl, 100) for wl in (BATCHED_8K, INTERVAL_16K, LONG_128K)}
+
     cpu = None
     if not a.no_cpu_baseline:
         log("bench: timing the CPU oracle")
@@ -442,6 +529,7 @@ def main() -> int:
                           "us_per_call": ms_mlp * 1e3, "algorithmic_bytes": mlp_bytes,
                           "achieved": mlp_gbs, "frac": mlp_gbs / PEAK_HBM_GBS},
         "offload": offload,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
