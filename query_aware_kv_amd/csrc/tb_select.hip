@@ -5,8 +5,10 @@
 // tokens under a fixed budget B.  Inference Strategy > Optimizations: neighbor
 // fetching widens each kept token t to [t-r, t+r].
 //
-// One 1024-thread work-group per (sequence, importance head).  Thread t owns
-// bitmap words w = t + 1024 j, i.e. the 32 positions 32w .. 32w+31.
+// One work-group per (sequence, importance head): 1024 threads, or 512 for
+// rows of up to 512 words on the 16-bit-key path (two such work-groups fit a
+// compute unit).  Thread t owns bitmap words w = t + THREADS j, i.e. the 32
+// positions 32w .. 32w+31.
 //   1. Scores become order-preserving u32 keys (-0 folded onto +0; positions
 //      >= n get key 0, below every real key).  Rows of up to 1024 words keep
 //      their keys in registers (read once, in 16-byte loads); longer rows
@@ -71,11 +73,12 @@ constexpr int kMiscList = 40;  // length of the list of keys sharing tau's 20-bi
 // Exclusive scan of popcount(words[w]) over w < nw into out[w] (skipped when
 // out is NULL); returns the total to every thread.  wsum: kSelWaves words of
 // LDS scratch.
+template <int THREADS>
 __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int nw,
                                       uint32_t *wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (nw + kSelThreads - 1) / kSelThreads;
+    const int per = (nw + THREADS - 1) / THREADS;
     const int w0 = tid * per;
     uint32_t local = 0;
     for (int w = w0; w < w0 + per && w < nw; ++w)
@@ -86,7 +89,7 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
     __syncthreads();
     uint32_t before = 0u, total = 0u;
 #pragma unroll
-    for (int v = 0; v < kSelWaves; ++v) {
+    for (int v = 0; v < (THREADS / 64); ++v) {
         const uint32_t x = wsum[v];
         before += v < wave ? x : 0u;
         total += x;
@@ -105,11 +108,12 @@ __device__ uint32_t block_popc_exscan(const uint32_t *words, uint32_t *out, int 
 // Writes the positions of the set bits of words[0..nw) in ascending order.
 // Set bits over nw words, the whole work-group (one barrier; wsum:
 // kSelWaves words, not reused afterwards).
+template <int THREADS>
 __device__ uint32_t block_popc_total(const uint32_t *words, int nw, uint32_t *wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint32_t local = 0u;
-    for (int w = tid; w < nw; w += kSelThreads)
+    for (int w = tid; w < nw; w += THREADS)
         local += __popc(words[w]);
     const uint32_t t = wave_reduce(local, [](uint32_t x, uint32_t y) { return x + y; });
     if (lane == 0)
@@ -117,14 +121,15 @@ __device__ uint32_t block_popc_total(const uint32_t *words, int nw, uint32_t *ws
     __syncthreads();
     uint32_t total = 0u;
 #pragma unroll
-    for (int v = 0; v < kSelWaves; ++v)
+    for (int v = 0; v < (THREADS / 64); ++v)
         total += wsum[v];
     return total;
 }
 
+template <int THREADS>
 __device__ void compact_bits(const uint32_t *words, const uint32_t *offs, int nw, int32_t *dst)
 {
-    for (int w = threadIdx.x; w < nw; w += kSelThreads) {
+    for (int w = threadIdx.x; w < nw; w += THREADS) {
         uint32_t bits = words[w];
         int pos = (int)offs[w];
         while (bits) {
@@ -273,8 +278,9 @@ __device__ __forceinline__ uint32_t mask_below(int w, int x)
     return c <= 0 ? 0u : (c >= 32 ? 0xFFFFFFFFu : (1u << c) - 1u);
 }
 
-template <int WPT, bool K16>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+template <int WPT, bool K16, int THREADS>
+__global__ __launch_bounds__(THREADS)
+__attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx_len, int Himp, int cap,
     int nwc, int B, int r, int32_t *__restrict__ sel_idx, int sel_stride,
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
@@ -283,6 +289,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint16_t *__restrict__ sample16, int s16)
 {
     static_assert(!K16 || WPT == 1, "16-bit first pass: one word per thread");
+    static_assert(THREADS == 1024 || (THREADS == 512 && K16), "1024 threads, or 512 on rows of <= 512 words");
+    constexpr int NWAVES = THREADS / 64;
     extern __shared__ __align__(16) uint32_t lds[];
     uint32_t *hist = lds;                         // [kCopies][kCopyStride]
     uint32_t *tot = hist + kCopies * kCopyStride; // [256]
@@ -327,9 +335,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     }
     // LDS that starts at zero (radix and sample histograms, misc words),
     // cleared before anything depends on the context length
-    for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+    for (int e = tid; e < kCopies * kCopyStride; e += THREADS)
         hist[e] = 0u;
-    for (int e = tid; e < kSampleBins; e += kSelThreads)
+    for (int e = tid; e < kSampleBins; e += THREADS)
         reinterpret_cast<uint32_t *>(cpair)[e] = 0u;
     if (tid < 64)
         misc[tid] = 0u;
@@ -340,12 +348,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         if (tid == 0)
             sel_count[rowid] = 0;
         if (sel_bits != nullptr)
-            for (int w = tid; w < bits_stride; w += kSelThreads)
+            for (int w = tid; w < bits_stride; w += THREADS)
                 sel_bits[rowid * bits_stride + w] = 0u;
         return;
     }
     const int nw = (n + 31) >> 5;
-    const int nwt = (nw + kSelThreads - 1) / kSelThreads; // words per thread
+    const int nwt = (nw + THREADS - 1) / THREADS; // words per thread
     const bool vec = (cap & 3) == 0; // every row starts 16-byte aligned
     // the sink [0, lo) and the local window [hi, n) are kept outright; the
     // budget goes to the middle region [lo, hi)
@@ -369,8 +377,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         } else {
             for (int j = 0; j < nwt; ++j) {
                 uint32_t k[32];
-                load_word_keys(row, tid + j * kSelThreads, lo, hi, n, vec, k);
-                fn(tid + j * kSelThreads, k);
+                load_word_keys(row, tid + j * THREADS, lo, hi, n, vec, k);
+                fn(tid + j * THREADS, k);
             }
         }
     };
@@ -447,7 +455,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     for (int q = 0; q < 4; ++q)
                         s4[q] = keys[8 * q];
                 } else {
-                    const int p0 = (tid + j * kSelThreads) * 32;
+                    const int p0 = (tid + j * THREADS) * 32;
                     float f[4];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
@@ -600,15 +608,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             na = wave_reduce(na, [](uint32_t x, uint32_t y) { return x + y; });
             if (lane == 0) {
                 tot[wave] = run;
-                tot[kSelWaves + wave] = na;
+                tot[NWAVES + wave] = na;
             }
             __syncthreads();
             uint32_t A = 0u, C = 0u;
             bool over = false;
 #pragma unroll
-            for (int v = 0; v < kSelWaves; ++v) {
+            for (int v = 0; v < NWAVES; ++v) {
                 C += tot[v];
-                A += tot[kSelWaves + v];
+                A += tot[NWAVES + v];
                 over |= tot[v] > (uint32_t)kWaveCap;
             }
             found = lvl && !over && A < (uint32_t)B && (uint32_t)B <= A + C;
@@ -677,10 +685,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 } else {
                     // many keys share the prefix: a histogram of their low
                     // 12 bits finds tau, then every candidate is placed
-                    for (int e = tid; e < kSampleBins; e += kSelThreads)
+                    for (int e = tid; e < kSampleBins; e += THREADS)
                         hist[e] = 0u;
                     __syncthreads();
-                    for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                    for (int i = tid; i < NWAVES * kWaveCap; i += THREADS) {
                         if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
                             const uint32_t kc = cpair[i].x;
                             if ((kc >> 12) == p20)
@@ -704,7 +712,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                     // candidates at or above tau join the kept words; those
                     // equal to tau are ties when ties are split
                     const bool split = need < cnt_eq;
-                    for (int i = tid; i < kSelWaves * kWaveCap; i += kSelThreads) {
+                    for (int i = tid; i < NWAVES * kWaveCap; i += THREADS) {
                         if ((uint32_t)(i % kWaveCap) < tot[i / kWaveCap]) {
                             const uint2 c = cpair[i];
                             const uint32_t bit = 1u << (c.y & 31u);
@@ -718,7 +726,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 }
                 emitted = true;
             } else {
-                for (int e = tid; e < kCopies * kCopyStride; e += kSelThreads)
+                for (int e = tid; e < kCopies * kCopyStride; e += THREADS)
                     hist[e] = 0u;
                 __syncthreads();
             }
@@ -795,8 +803,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         __syncthreads();
     }
     if (partial_ties) {
-        block_popc_exscan(Sb, scan, nw, misc + kMiscScan);
-        for (int w = tid; w < nw; w += kSelThreads) {
+        block_popc_exscan<THREADS>(Sb, scan, nw, misc + kMiscScan);
+        for (int w = tid; w < nw; w += THREADS) {
             uint32_t e = Sb[w];
             const uint32_t pre = scan[w];
             if (pre >= need) {
@@ -814,8 +822,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
     // ---- optional pre-widening output ----
     if (topb_idx != nullptr) {
-        block_popc_exscan(Tb, scan, nw, misc + kMiscScan);
-        compact_bits(Tb, scan, nw, topb_idx + rowid * (size_t)B);
+        block_popc_exscan<THREADS>(Tb, scan, nw, misc + kMiscScan);
+        compact_bits<THREADS>(Tb, scan, nw, topb_idx + rowid * (size_t)B);
         __syncthreads();
     }
 
@@ -827,7 +835,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         int left = r;
         while (left > 0) {
             const int step = left < 31 ? left : 31;
-            for (int w = tid; w < nw; w += kSelThreads) {
+            for (int w = tid; w < nw; w += THREADS) {
                 const uint32_t x = src[w];
                 const uint32_t prv = w > 0 ? src[w - 1] : 0u;
                 const uint32_t nxt = w + 1 < nw ? src[w + 1] : 0u;
@@ -848,19 +856,19 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
     // ---- the sink and the local window join the set ----
     if (lo > 0 || hi < n) {
-        for (int w = tid; w < nw; w += kSelThreads)
+        for (int w = tid; w < nw; w += THREADS)
             fin[w] |= mask_below(w, lo) | (mask_below(w, n) & ~mask_below(w, hi));
         __syncthreads();
     }
 
     // ---- |S|, the ascending list (when asked) and the bitmap (when asked) ----
     const uint32_t total = sel_idx != nullptr
-                               ? block_popc_exscan(fin, scan, nw, misc + kMiscScan)
-                               : block_popc_total(fin, nw, misc + kMiscScan);
+                               ? block_popc_exscan<THREADS>(fin, scan, nw, misc + kMiscScan)
+                               : block_popc_total<THREADS>(fin, nw, misc + kMiscScan);
     if (sel_idx != nullptr)
-        compact_bits(fin, scan, nw, sel_idx + rowid * sel_stride);
+        compact_bits<THREADS>(fin, scan, nw, sel_idx + rowid * sel_stride);
     if (sel_bits != nullptr)
-        for (int w = tid; w < bits_stride; w += kSelThreads)
+        for (int w = tid; w < bits_stride; w += THREADS)
             sel_bits[rowid * bits_stride + w] = w < nw ? fin[w] : 0u;
     if (tid == 0)
         sel_count[rowid] = (int32_t)total;
@@ -869,15 +877,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 // words per bitmap array, even so that the candidate pairs stay 8-byte aligned
 inline int sel_words(int cap) { return ((cap + 31) / 32 + 2) & ~1; }
 // dynamic LDS of one selection work-group
-inline size_t sel_lds_bytes(int cap)
+inline size_t sel_lds_bytes(int cap, int waves)
 {
     const size_t nwc = (size_t)sel_words(cap);
-    const size_t u = 2 * nwc > 2 * (size_t)kSelWaves * kWaveCap ? 2 * nwc
-                                                                 : 2 * (size_t)kSelWaves * kWaveCap;
+    const size_t u = 2 * nwc > 2 * (size_t)waves * kWaveCap ? 2 * nwc
+                                                             : 2 * (size_t)waves * kWaveCap;
     return ((size_t)kCopies * kCopyStride + 256 + 64 + 2 * nwc + u) * sizeof(uint32_t);
 }
 
-template <int WPT, bool K16>
+// Rows of up to 512 words (16K positions, a sample of at most 2048 keys)
+// take the 16-bit-key selection in 512-thread work-groups, two of which fit
+// a compute unit; longer rows take 1024 threads, one word per thread.
+constexpr int kSelShortCap = 16384;
+
+template <int WPT, bool K16, int THREADS>
 hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *scores,
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                     int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
@@ -885,7 +898,7 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
                     const uint16_t *sample16, hipStream_t st)
 {
     const int nwc = sel_words(s.ctx_cap);
-    const size_t lds = sel_lds_bytes(s.ctx_cap);
+    const size_t lds = sel_lds_bytes(s.ctx_cap, THREADS / 64);
     if (lds > 64 * 1024) {
         // the launch limit is raised once per device, to what the largest
         // capacity needs
@@ -896,16 +909,16 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
             return e;
         const uint64_t bit = dev < 64 ? 1ull << dev : 0ull;
         if (bit == 0ull || (raised.load(std::memory_order_relaxed) & bit) == 0ull) {
-            e = hipFuncSetAttribute((const void *)select_kernel<WPT, K16>,
+            e = hipFuncSetAttribute((const void *)select_kernel<WPT, K16, THREADS>,
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)sel_lds_bytes(kMaxCtxCap));
+                                    (int)sel_lds_bytes(kMaxCtxCap, THREADS / 64));
             if (e != hipSuccess)
                 return e;
             raised.fetch_or(bit, std::memory_order_relaxed);
         }
     }
     dim3 grid(s.n_imp_heads, s.batch);
-    hipLaunchKernelGGL((select_kernel<WPT, K16>), grid, dim3(kSelThreads), lds, st, scores,
+    hipLaunchKernelGGL((select_kernel<WPT, K16, THREADS>), grid, dim3(THREADS), lds, st, scores,
                        ctx_len, s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx,
                        sel_stride, sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap),
                        keep_from, n_new, p.n_sink, p.n_local, keys16, sample16,
@@ -925,12 +938,17 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
     s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from,       \
         n_new, keys16, sample16, st
     static_assert(kSelThreads == 1024, "select_key16: one word per thread up to 1024 words");
+    static_assert(kSelShortCap / 32 <= 512 && kSelShortCap / 8 <= 4 * 512,
+                  "short rows: one word and four sample keys per thread of 512");
     if (select_key16(s.ctx_cap)) {
-        if (keys16 != nullptr && sample16 != nullptr)
-            return select_t<1, true>(TB_SEL_ARGS);
-        return select_t<1, false>(TB_SEL_ARGS);
+        if (keys16 != nullptr && sample16 != nullptr) {
+            if (s.ctx_cap <= kSelShortCap)
+                return select_t<1, true, 512>(TB_SEL_ARGS);
+            return select_t<1, true, 1024>(TB_SEL_ARGS);
+        }
+        return select_t<1, false, 1024>(TB_SEL_ARGS);
     }
-    return select_t<0, false>(TB_SEL_ARGS);
+    return select_t<0, false, 1024>(TB_SEL_ARGS);
 #undef TB_SEL_ARGS
 }
 

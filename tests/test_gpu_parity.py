@@ -164,6 +164,25 @@ def test_fused_step_odd_capacity(kw):
         assert float(np.abs(f64(out[b]) - ref).max()) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("ctx0", [16383, 16384], ids=["cap16384", "cap16385"])
+def test_fused_step_selection_block_sizes(ctx0):
+    # the fused step selects rows of up to 16384 positions with 512 threads
+    # (every thread holding one 32-position word and four sample keys at
+    # 16384) and longer rows with 1024
+    w = _small(ctx0=ctx0, batch=2, budget=1600)
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in range(w.batch):
+        st = oracle_state(w, dc.pre, b)
+        ref = oracle_step(w, st, dc.pre, inp, 0, b)
+        got = lists_of(dc.sel, dc.cnt, b)
+        for i in range(w.n_imp_heads):
+            assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
+        assert float(np.abs(f64(out[b]) - ref).max()) <= TOL[w.dtype]
+
+
 def test_planted_tokens_are_found():
     # sanity of the synthetic workload, not a parity bar: with a shift of 4
     # score standard deviations nearly every planted token is selected
