@@ -23,8 +23,8 @@
 //      select are requested by sibling waves of the same work-group, and the
 //      repeats are served from L2 as long as the siblings stay close.  With
 //      one work-group per compute unit they do.  With several per unit each
-//      head's waves run at their own pace and drift apart, so there (bitmaps,
-//      16-bit rows of 128) the waves walk their parts in steps of 128
+//      head's waves run at their own pace and drift apart, so there (16-bit
+//      rows of 128) the waves walk their parts in steps of 128
 //      positions with a work-group barrier after each step.
 //   3. Rows stream through the lanes in 16-byte pieces (D*elt/16 lanes per
 //      row, several rows per wave, four rows in flight per row slot); each row
@@ -224,12 +224,12 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
     const int hw = wave / WPH, wpart = wave % WPH;
     constexpr int WPW = PW / 32;
     static_assert(WPW <= 64 && WPW % 2 == 0, "a part's words fit one wave, in pairs");
-    // Windowed walk (WIN > 0, bitmap mode): the waves cover their parts in
+    // Windowed walk (WIN > 0): the waves cover their parts in
     // steps of WIN word pairs and meet at a barrier after each step, so all
     // query heads of the group read a shared row within a short time of
     // each other and the later reads find it in L2.  wend holds the end of
     // each step in the wave's position list.
-    static_assert(WIN == 0 || (BITMAP && (WPW / 2) % WIN == 0), "whole steps per part");
+    static_assert(WIN == 0 || (WPW / 2) % WIN == 0, "whole steps per part");
     constexpr int NWIN = WIN > 0 ? WPW / 2 / WIN : 1;
     __shared__ uint16_t wend[kAttnWaves][NWIN];
     // Everything that does not depend on the lengths is requested first: the
@@ -463,8 +463,8 @@ hipError_t device_cus(int &cus)
     return hipSuccess;
 }
 
-template <typename T, int D, int GQ, bool APPEND>
-hipError_t attn_bitmap_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
+template <typename T, int D, int GQ, bool BITMAP, bool APPEND>
+hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
     const int nchunk = attn_chunks(s.ctx_cap);
     const dim3 grid = APPEND ? dim3((nchunk + 1) * s.n_kv_heads * s.batch)
@@ -483,11 +483,11 @@ hipError_t attn_bitmap_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
         windowed = wgs >= 2L * cus;
     if constexpr (attn_windowed_ok<T, D, GQ>())
         if (windowed)
-            hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, kAttnWindowPairs, APPEND>), grid,
+            hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, kAttnWindowPairs, APPEND>), grid,
                                dim3(kAttnThreads), 0, st, a);
     if (!windowed)
-        hipLaunchKernelGGL((attn_kernel<T, D, GQ, true, 0, APPEND>), grid, dim3(kAttnThreads), 0,
-                           st, a);
+        hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, 0, APPEND>), grid, dim3(kAttnThreads),
+                           0, st, a);
     return hipGetLastError();
 }
 
@@ -495,12 +495,9 @@ template <typename T, int D, int GQ>
 hipError_t attn_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
     if (a.sel_bits != nullptr)
-        return a.n_new > 0 ? attn_bitmap_t<T, D, GQ, true>(s, a, st)
-                           : attn_bitmap_t<T, D, GQ, false>(s, a, st);
-    const dim3 grid(attn_chunks(s.ctx_cap), s.n_kv_heads, s.batch);
-    hipLaunchKernelGGL((attn_kernel<T, D, GQ, false, 0, false>), grid, dim3(kAttnThreads), 0, st,
-                       a);
-    return hipGetLastError();
+        return a.n_new > 0 ? attn_launch_t<T, D, GQ, true, true>(s, a, st)
+                           : attn_launch_t<T, D, GQ, true, false>(s, a, st);
+    return attn_launch_t<T, D, GQ, false, false>(s, a, st);
 }
 
 template <typename T, int D>

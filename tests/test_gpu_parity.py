@@ -330,9 +330,13 @@ def test_windowed_attention_walk(kw):
     args = tbl.step_args(dc.shape, dc.params, q=inp.q.cuda(), q_imp=inp.q_imp.cuda(),
                          k_new=inp.k_new.cuda(), v_new=inp.v_new.cuda(), refresh=True, w=dc.W,
                          k_cache=dc.K, v_cache=dc.V, kp_cache=dc.Kp, ctx_len=ctx,
-                         softmax_scale=w.softmax_scale, sel_idx=None, sel_count=dc.cnt,
+                         softmax_scale=w.softmax_scale, sel_idx=dc.sel, sel_count=dc.cnt,
                          sel_bits=dc.bits, keep_from=dc.keep, out=out)
     tbl.decode_step(dc.shape, dc.params, args, dc.ws)
+    # the same attention from the index lists (contiguous chunks)
+    out_l = torch.empty_like(out)
+    tbl.sparse_attn(dc.shape, inp.q.cuda(), dc.K, dc.V, dc.sel, dc.cap_s, dc.cnt, dc.keep, ctx,
+                    w.softmax_scale, out_l, dc.ws)
     torch.cuda.synchronize()
     for b in (0, 1, 2, 3, w.batch - 1):
         n = lens[b]
@@ -345,6 +349,8 @@ def test_windowed_attention_walk(kw):
             assert got[i] == st.sel[i, :st.cnt[i]].tolist(), (b, i)
         err = float(np.abs(f64(out[b]) - ref).max())
         assert err <= TOL[w.dtype], (b, err)
+        err_l = float(np.abs(f64(out_l[b]) - ref).max())
+        assert err_l <= TOL[w.dtype], (b, err_l)
 
 
 @pytest.mark.parametrize("kw", [dict(steps=4), dict(steps=4, ctx0=7000, budget=300, batch=40,
