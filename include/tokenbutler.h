@@ -12,6 +12,9 @@
  *   [ABS]  TokenButler abstract, 2026 version (author page, searcharxiv.com)
  *   [ARCH] gist.science technical summary, Methodology > Core Architecture
  *   [INF]  gist.science technical summary, Inference Strategy > Optimizations
+ *   [RES]  gist.science technical summary, Key Contributions and Experimental
+ *          Results (the speedups against dense attention, on the GPU and with
+ *          the cache offloaded to CPU memory)
  *   [SIG]  gist.science technical summary, Significance
  *
  * Conventions shared by every call
@@ -116,8 +119,9 @@ const char *tb_strerror(int code);
  * Host only. */
 size_t tb_workspace_bytes(const tb_shape *shape, const tb_select_params *params);
 
-/* Capacity of one head's selected-index list: min(ctx_cap, (2r+1)*B).  The
- * sel_idx stride written by tb_select and tb_decode_step.  0 if invalid. */
+/* Capacity of one head's selected-index list:
+ * min(ctx_cap, (2r+1)*B + n_sink + n_local).  The sel_idx stride written by
+ * tb_select and tb_decode_step.  0 if invalid. */
 int32_t tb_selection_capacity(const tb_shape *shape, const tb_select_params *params);
 
 /* 32-bit words of one head's selection bitmap: ceil(ctx_cap / 32).  0 if the

@@ -51,6 +51,8 @@ def _load():
         lib.orc_score.argtypes = [P, P] + [ctypes.c_int] * 5 + [P, P]
         lib.orc_topb.argtypes = [P, i32, i32, P]
         lib.orc_topb.restype = i32
+        lib.orc_topb64.argtypes = [P, i32, i32, P]
+        lib.orc_topb64.restype = i32
         lib.orc_expand.argtypes = [P, i32, i32, i32, P]
         lib.orc_expand.restype = i32
         lib.orc_mlp.argtypes = [P, P, P] + [ctypes.c_int] * 8 + [P]
@@ -59,6 +61,8 @@ def _load():
         lib.orc_buffers.restype = None
         lib.orc_select.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
         lib.orc_select.restype = i32
+        lib.orc_select64.argtypes = [P, i32, i32, i32, i32, i32, P, P, P]
+        lib.orc_select64.restype = i32
         lib.orc_attend.argtypes = [P, P, P, ctypes.c_int, P, i32, dbl, P, P]
         lib.orc_decode_step.argtypes = (
             [ctypes.c_int] * 7 + [P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, P, P,
@@ -129,6 +133,16 @@ def topb(s32, B: int) -> np.ndarray:
     return T[:c].copy()
 
 
+def topb64(s64, B: int) -> np.ndarray:
+    """Ascending indices of the top-B entries of fp64 scores (score desc,
+    index asc): the ranking of the exact dot products."""
+    s = _f64(s64)
+    n = s.size
+    T = np.empty(max(n, 1), dtype=np.int32)
+    c = _load().orc_topb64(_p(s), n, int(B), _p(T))
+    return T[:c].copy()
+
+
 def expand(T, n: int, r: int) -> np.ndarray:
     """Sorted union of [t-r, t+r] clipped to [0, n) over t in T."""
     T = _i32(T)
@@ -188,6 +202,18 @@ def select(s32, B: int, r: int, n_sink: int = 0, n_local: int = 0):
     nT = ctypes.c_int32()
     c = _load().orc_select(_p(s), n, int(B), int(r), int(n_sink), int(n_local), _p(T),
                            ctypes.byref(nT), _p(S))
+    return T[:nT.value].copy(), S[:c].copy()
+
+
+def select64(s64, B: int, r: int, n_sink: int = 0, n_local: int = 0):
+    """As :func:`select`, ranking fp64 scores (the exact dot products)."""
+    s = _f64(s64)
+    n = s.size
+    T = np.empty(max(n, 1), dtype=np.int32)
+    S = np.empty(max(n, 1), dtype=np.int32)
+    nT = ctypes.c_int32()
+    c = _load().orc_select64(_p(s), n, int(B), int(r), int(n_sink), int(n_local), _p(T),
+                             ctypes.byref(nT), _p(S))
     return T[:nT.value].copy(), S[:c].copy()
 
 

@@ -26,7 +26,10 @@
  *     coordinates in ascending order, starting from +0.  (The pages fix no
  *     precision; a floating-point result that decides an integer -- here the
  *     kept set -- is taken in the same precision on both sides.)  The exact
- *     fp64 dot product is reported beside it for accuracy checks.
+ *     fp64 dot product is reported beside it, and orc_topb64 / orc_select64
+ *     rank those fp64 values: the selection the method defines, which the
+ *     tests hold the GPU sets to outside a 1e-6 relative band around the
+ *     B-th score (the fp32 chain is the stricter, bit-exact second check).
  *   - Top-B orders tokens by (score descending, index ascending).  -0 and +0
  *     tie.  If B >= n every token is kept.
  *   - Neighbor fetching widens every kept token t to [t-r, t+r] clipped to
@@ -147,7 +150,7 @@ void orc_score(const double *q_imp, const double *Kp, int Himp, int Hkv, int cap
 /* ------------------------------------------------------------------ */
 
 typedef struct {
-    float s;
+    double s;
     int32_t t;
 } orc_key;
 
@@ -162,8 +165,9 @@ static int orc_key_cmp(const void *a, const void *b)
 }
 
 /* T = the first min(B, n) tokens in (score desc, index asc) order, written
- * in ascending index order.  Returns |T|. */
-int32_t orc_topb(const float *s, int32_t n, int32_t B, int32_t *T)
+ * in ascending index order.  Returns |T|.  Scores are compared as doubles:
+ * -0 and +0 compare equal, so they tie and the lower index wins. */
+int32_t orc_topb64(const double *s, int32_t n, int32_t B, int32_t *T)
 {
     if (n <= 0 || B <= 0)
         return 0;
@@ -183,6 +187,20 @@ int32_t orc_topb(const float *s, int32_t n, int32_t B, int32_t *T)
             T[c++] = t;
     free(keep);
     free(a);
+    return c;
+}
+
+/* The same ranking of fp32 scores (every float converts to double exactly,
+ * so the order is the float order). */
+int32_t orc_topb(const float *s, int32_t n, int32_t B, int32_t *T)
+{
+    if (n <= 0 || B <= 0)
+        return 0;
+    double *d = (double *)malloc((size_t)n * sizeof(double));
+    for (int32_t t = 0; t < n; ++t)
+        d[t] = (double)s[t];
+    int32_t c = orc_topb64(d, n, B, T);
+    free(d);
     return c;
 }
 
@@ -271,12 +289,12 @@ void orc_buffers(int32_t n, int32_t n_sink, int32_t n_local, int32_t *lo, int32_
     *hi = b;
 }
 
-/* One head's kept set S over a context of n tokens: the important buffer is
- * the top-B tokens of the middle region (T, written to T when not NULL),
- * widened by r; S is its union with the sink and the local window, in
- * ascending order.  Returns |S|; *nT receives |T|. */
-int32_t orc_select(const float *s, int32_t n, int32_t B, int32_t r, int32_t n_sink,
-                   int32_t n_local, int32_t *T, int32_t *nT, int32_t *S)
+/* One head's kept set S over a context of n tokens (fp64 scores s): the
+ * important buffer is the top-B tokens of the middle region (T, written to
+ * T when not NULL), widened by r; S is its union with the sink and the local
+ * window, in ascending order.  Returns |S|; *nT receives |T|. */
+int32_t orc_select64(const double *s, int32_t n, int32_t B, int32_t r, int32_t n_sink,
+                     int32_t n_local, int32_t *T, int32_t *nT, int32_t *S)
 {
     if (n <= 0) {
         *nT = 0;
@@ -287,7 +305,7 @@ int32_t orc_select(const float *s, int32_t n, int32_t B, int32_t r, int32_t n_si
     int32_t *Tm = (int32_t *)malloc((size_t)n * sizeof(int32_t));
     int32_t *E = (int32_t *)malloc((size_t)n * sizeof(int32_t));
     /* 1. important buffer: top-B of the middle region, back in context positions */
-    int32_t m = orc_topb(s + lo, hi - lo, B, Tm);
+    int32_t m = orc_topb64(s + lo, hi - lo, B, Tm);
     for (int32_t k = 0; k < m; ++k)
         Tm[k] += lo;
     /* 2. neighbor fetching */
@@ -310,6 +328,18 @@ int32_t orc_select(const float *s, int32_t n, int32_t B, int32_t r, int32_t n_si
     free(in);
     free(E);
     free(Tm);
+    return c;
+}
+
+/* orc_select on fp32 scores (ranked as their exact double values). */
+int32_t orc_select(const float *s, int32_t n, int32_t B, int32_t r, int32_t n_sink,
+                   int32_t n_local, int32_t *T, int32_t *nT, int32_t *S)
+{
+    double *d = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    for (int32_t t = 0; t < n; ++t)
+        d[t] = (double)s[t];
+    int32_t c = orc_select64(d, n, B, r, n_sink, n_local, T, nT, S);
+    free(d);
     return c;
 }
 

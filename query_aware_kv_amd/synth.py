@@ -58,17 +58,22 @@ def draw_w(w: Workload, layer: int = 0) -> torch.Tensor:
     return _to_dtype(z.astype(np.float64) / np.sqrt(w.head_dim), w)
 
 
-def draw_q_imp(w: Workload, step: int, layer: int = 0) -> torch.Tensor:
-    """Importance queries of decode step ``step``: [b][H_imp][d]."""
+def _items(w: Workload, items) -> list[int]:
+    return list(range(w.batch)) if items is None else [int(b) for b in items]
+
+
+def draw_q_imp(w: Workload, step: int, layer: int = 0, items=None) -> torch.Tensor:
+    """Importance queries of decode step ``step``: [b][H_imp][d] (the batch
+    items ``items``, default all)."""
     z = np.stack([_normal(w, (w.n_imp_heads, w.d_imp), QIMP_ID, layer, b, step + 1)
-                  for b in range(w.batch)])
+                  for b in _items(w, items)])
     return _to_dtype(z, w)
 
 
-def draw_q(w: Workload, step: int, layer: int = 0) -> torch.Tensor:
+def draw_q(w: Workload, step: int, layer: int = 0, items=None) -> torch.Tensor:
     """Attention queries of decode step ``step``: [b][Hq][D]."""
     z = np.stack([_normal(w, (w.n_q_heads, w.head_dim), Q_ID, layer, b, step + 1)
-                  for b in range(w.batch)])
+                  for b in _items(w, items)])
     return _to_dtype(z, w)
 
 
@@ -105,18 +110,19 @@ class Prefill:
     planted: dict = field(default_factory=dict)
 
 
-def prefill(w: Workload, layer: int = 0) -> Prefill:
+def prefill(w: Workload, layer: int = 0, items=None) -> Prefill:
     Hkv, D, cap = w.n_kv_heads, w.head_dim, w.ctx_cap
     single = w.steps == 1
     rows = w.ctx0 + 1 if single else w.ctx0
+    its = _items(w, items)
     W = draw_w(w, layer)
-    q_imp0 = draw_q_imp(w, 0, layer)
+    q_imp0 = draw_q_imp(w, 0, layer, its)
     W64 = W.to(torch.float64).numpy()
     qi64 = q_imp0.to(torch.float64).numpy()
-    K = torch.zeros((w.batch, Hkv, cap, D), dtype=torch_dtype(w))
+    K = torch.zeros((len(its), Hkv, cap, D), dtype=torch_dtype(w))
     V = torch.zeros_like(K)
     planted = {}
-    for b in range(w.batch):
+    for j, b in enumerate(its):
         k32 = _normal(w, (Hkv, rows, D), K_ID, layer, b, 0)
         v32 = _normal(w, (Hkv, rows, D), V_ID, layer, b, 0)
         shifts: dict[tuple[int, int], np.ndarray] = {}
@@ -126,15 +132,15 @@ def prefill(w: Workload, layer: int = 0) -> Prefill:
             if pos.size == 0:
                 continue
             g = i * Hkv // w.n_imp_heads
-            u = W64 @ qi64[b, i]
+            u = W64 @ qi64[j, i]
             u = u / np.linalg.norm(u)
             for t in pos.tolist():
                 key = (g, t)
                 shifts[key] = shifts.get(key, 0.0) + w.plant_shift * u
         for (g, t), delta in shifts.items():
             k32[g, t] = (k32[g, t].astype(np.float64) + delta).astype(np.float32)
-        K[b, :, :rows] = _to_dtype(k32, w)
-        V[b, :, :rows] = _to_dtype(v32, w)
+        K[j, :, :rows] = _to_dtype(k32, w)
+        V[j, :, :rows] = _to_dtype(v32, w)
     k_next = v_next = None
     if single:
         k_next = K[:, :, w.ctx0:w.ctx0 + 1].clone()
@@ -154,18 +160,20 @@ class StepInputs:
     refresh: bool
 
 
-def step_inputs(w: Workload, s: int, pre: Prefill, layer: int = 0) -> StepInputs:
-    """Inputs of decode step s (token appended at position ctx0 + s)."""
+def step_inputs(w: Workload, s: int, pre: Prefill, layer: int = 0, items=None) -> StepInputs:
+    """Inputs of decode step s (token appended at position ctx0 + s) for the
+    batch items of ``pre`` (``items``, default all)."""
     refresh = s % w.interval == 0
+    its = _items(w, items)
     if w.steps == 1:
         k_new, v_new = pre.k_next, pre.v_next
     else:
         k_new = torch.stack([_to_dtype(_normal(w, (w.n_kv_heads, 1, w.head_dim), K_ID, layer,
-                                               b, s + 1), w) for b in range(w.batch)])
+                                               b, s + 1), w) for b in its])
         v_new = torch.stack([_to_dtype(_normal(w, (w.n_kv_heads, 1, w.head_dim), V_ID, layer,
-                                               b, s + 1), w) for b in range(w.batch)])
-    q = draw_q(w, s, layer)
-    q_imp = (pre.q_imp0 if s == 0 else draw_q_imp(w, s, layer)) if refresh else None
+                                               b, s + 1), w) for b in its])
+    q = draw_q(w, s, layer, its)
+    q_imp = (pre.q_imp0 if s == 0 else draw_q_imp(w, s, layer, its)) if refresh else None
     return StepInputs(k_new=k_new, v_new=v_new, q=q, q_imp=q_imp, refresh=refresh)
 
 

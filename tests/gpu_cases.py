@@ -15,8 +15,11 @@ import oracle as orc
 from query_aware_kv_amd import synth
 from query_aware_kv_amd import tokenbutler as tbl
 from query_aware_kv_amd.workloads import Workload
+from tests.tolerances import TOL, bf16_bound
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+# relative width of the ambiguity band around the B-th score: tokens whose
+# exact (fp64) score lies this close to it may be decided either way
+BAND_REL = 1e-6
 
 
 def need_gpu():
@@ -131,9 +134,88 @@ def bitmap_positions(bits: torch.Tensor, b: int, n: int) -> list:
     return out
 
 
-def band_members(s32: np.ndarray, B: int, rel: float = 1e-6) -> np.ndarray:
+def band_members(s: np.ndarray, B: int, rel: float = BAND_REL) -> np.ndarray:
     """Tokens whose score lies within rel * |tau| of the B-th largest score."""
-    if B >= s32.size:
+    if B >= s.size:
         return np.zeros(0, dtype=np.int64)
-    tau = np.sort(s32.astype(np.float64))[::-1][B - 1]
-    return np.nonzero(np.abs(s32.astype(np.float64) - tau) <= rel * abs(tau))[0]
+    s = s.astype(np.float64)
+    tau = np.sort(s)[::-1][B - 1]
+    return np.nonzero(np.abs(s - tau) <= rel * abs(tau))[0]
+
+
+def fp64_selection(s64: np.ndarray, n: int, B: int, r: int, n_sink: int = 0, n_local: int = 0):
+    """The selection of the exact (fp64) scores of one head over [0, n):
+    (T64, S64, band, U).  band: the middle-region tokens whose fp64 score is
+    within BAND_REL of the B-th one (empty when the budget covers the
+    region); U: the positions within r of a band member, whose membership in
+    the widened set a band member can change."""
+    T64, S64 = orc.select64(s64[:n], B, r, n_sink, n_local)
+    lo, hi = orc.buffers(n, n_sink, n_local)
+    band = lo + band_members(s64[lo:hi], B)
+    U = np.zeros(max(n, 1), dtype=bool)
+    for a in band.tolist():
+        U[max(0, a - r):min(n, a + r + 1)] = True
+    return T64, S64, band, U[:n]
+
+
+def assert_fp64_selection(S_gpu, s64: np.ndarray, n: int, B: int, r: int, n_sink: int = 0,
+                          n_local: int = 0, T_gpu=None, what=()) -> int:
+    """The comparator of selected sets against the exact scores: the GPU's
+    widened set equals the fp64 one at every position no band member can
+    reach, and, when the pre-widening set is given, it has the same size as
+    the fp64 top-B and the same members outside the band.  Returns the band
+    size (logged by the callers)."""
+    T64, S64, band, U = fp64_selection(s64, n, B, r, n_sink, n_local)
+    got = np.zeros(n, dtype=bool)
+    ref = np.zeros(n, dtype=bool)
+    got[np.asarray(S_gpu, dtype=np.int64)] = True
+    ref[S64] = True
+    diff = np.nonzero((got != ref) & ~U)[0]
+    assert diff.size == 0, ("widened set differs from the fp64 selection outside the band",
+                            what, diff[:10].tolist(), band.tolist())
+    if T_gpu is not None:
+        T_gpu = np.asarray(T_gpu, dtype=np.int64)
+        assert T_gpu.size == T64.size, ("|T| differs from the fp64 top-B", what)
+        bset = set(band.tolist())
+        assert set(T_gpu.tolist()) - bset == set(T64.tolist()) - bset, (
+            "top-B differs from the fp64 top-B outside the band", what)
+    return int(band.size)
+
+
+def attended_sets(w: Workload, st: orc.SequenceState, n: int) -> list:
+    """Per query head, the positions the oracle's state attends at context n."""
+    kf = max(int(st.keep_from[0]), 0)
+    out = []
+    for h in range(w.n_q_heads):
+        i = h * w.n_imp_heads // w.n_q_heads
+        A = {int(t) for t in st.sel[i, :st.cnt[i]] if t < n} | set(range(kf, n))
+        out.append(sorted(A))
+    return out
+
+
+def oracle_attention(w: Workload, K: np.ndarray, V: np.ndarray, q: np.ndarray, sets) -> tuple:
+    """(o_ref [Hq, D], bound [Hq, D]) over the given attended sets (K, V
+    [Hkv, cap, D] fp64); bound is the derived bf16 bound of each element."""
+    o = np.zeros((w.n_q_heads, w.head_dim))
+    bound = np.zeros_like(o)
+    for h, A in enumerate(sets):
+        g = h * w.n_kv_heads // w.n_q_heads
+        A = np.asarray(A, dtype=np.int32)
+        o[h], wts = orc.attend(q[h], K[g], V[g], A, w.softmax_scale, return_weights=True)
+        bound[h] = bf16_bound(o[h], wts, V[g][A]) if A.size else 0.0
+    return o, bound
+
+
+def assert_attention(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, dtype: str,
+                     what=()) -> float:
+    """Contract bar (max-abs 1e-4 fp32 / 2e-2 bf16) and, for bf16, the derived
+    per-element bound.  Returns the largest error / bound ratio (bf16) or the
+    max-abs error (fp32)."""
+    err = np.abs(got - ref)
+    assert float(err.max(initial=0.0)) <= TOL[dtype], ("contract bar", what, float(err.max()))
+    if dtype != "bf16":
+        return float(err.max(initial=0.0))
+    bad = err > bound
+    assert not bad.any(), ("derived bf16 bound", what, float((err / np.maximum(bound, 1e-300)).max()),
+                           np.argwhere(bad)[:5].tolist())
+    return float((err / np.maximum(bound, 1e-300)).max(initial=0.0))

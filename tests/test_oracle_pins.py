@@ -252,6 +252,44 @@ def test_topb_brute_force_rank_count(seed):
         assert orc.topb(s, B).tolist() == _rank_count_topb(s, B)
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_topb64_brute_force_rank_count(seed):
+    # the fp64 ranking (the selection of the exact dot products): the same
+    # rank-count definition on doubles, with pairs that differ only below
+    # float precision, so a ranking that went through fp32 would tie them
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 65))
+    if seed % 3 == 0:
+        s = rng.standard_normal(n)
+    elif seed % 3 == 1:     # tie-heavy, with signed zeros
+        s = rng.choice(np.array([-1.0, -0.0, 0.0, 0.5, 2.0]), size=n)
+    else:                   # values 2^-40 apart: distinct in fp64, equal in fp32
+        s = 1.0 + rng.integers(0, 4, size=n) * 2.0 ** -40
+        assert np.unique(s.astype(np.float32)).size == 1
+    for B in {1, 2, n // 2 + 1, n, n + 3}:
+        assert orc.topb64(s, B).tolist() == _rank_count_topb(s, B)
+
+
+def test_select64_brute_force_with_buffers():
+    # select64 = rank-count top-B of the fp64 middle region, widened, united
+    # with the sink and the local window (each step written out by hand here)
+    rng = np.random.default_rng(760)
+    for _ in range(25):
+        n = int(rng.integers(1, 70))
+        s = 1.0 + rng.integers(0, 5, size=n) * 2.0 ** -45 + rng.standard_normal(n) * (
+            rng.random() < 0.5)
+        B, r = int(rng.integers(1, 12)), int(rng.integers(0, 3))
+        ns, nl = int(rng.integers(0, 6)), int(rng.integers(0, 6))
+        lo = min(ns, n)
+        hi = max(lo, n - nl)
+        T = [lo + t for t in _rank_count_topb(s[lo:hi], B)]
+        S = set(range(lo)) | set(range(hi, n))
+        for t in T:
+            S |= set(range(max(0, t - r), min(n, t + r + 1)))
+        T_o, S_o = orc.select64(s, B, r, ns, nl)
+        assert T_o.tolist() == T and S_o.tolist() == sorted(S)
+
+
 def test_topb_golden_hand_cases():
     for c in _golden("topb_cases.json")["cases"]:
         s = np.array([float(v) for v in c["scores"]], dtype=np.float32)
@@ -560,6 +598,39 @@ def test_interval_golden_hand_case(name):
         np.testing.assert_allclose(out[0], expect, atol=1e-15)
         assert st.sel[0, :st.cnt[0]].tolist() == g["stored_by_step"][s]
         assert int(st.keep_from[0]) == g["keep_from_by_step"][s]
+
+
+def test_refresh_with_several_new_rows_golden_hand_case():
+    # steps that append three rows each: the refresh scores the new rows with
+    # the rest, and keep_from = ctx - n_new keeps all three attended
+    g = _golden("interval_multirow_case.json")
+    scores = g["scores_by_position"]
+    D = 16
+    K, V, W = _one_hot_sequence(scores, D)
+    ctx0, nn = g["ctx0"], g["n_new"]
+    cap = len(scores)
+    Kc = np.zeros((1, cap, D))
+    Vc = np.zeros((1, cap, D))
+    Kc[0, :ctx0] = K[:ctx0]
+    Vc[0, :ctx0] = V[:ctx0]
+    for r_key in ("radius_0", "radius_1"):
+        case = g[r_key]
+        st = orc.SequenceState(Kc, Vc, orc.project(Kc, W, orc.F32), Himp=1, B=g["budget"],
+                               r=case["radius"])
+        for s_, attended in enumerate(case["attended_by_step"]):
+            ctx = ctx0 + (s_ + 1) * nn
+            refresh = s_ % g["interval"] == 0
+            out = orc.decode_step(st, W, np.zeros((1, D)), np.ones((1, 1)), ctx, orc.F32,
+                                  refresh, 1.0, k_new=K[None, ctx - nn:ctx],
+                                  v_new=V[None, ctx - nn:ctx])
+            expect = np.zeros(D)
+            expect[attended] = 1.0 / len(attended)
+            np.testing.assert_allclose(out[0], expect, atol=1e-15)
+            assert st.sel[0, :st.cnt[0]].tolist() == case["stored_by_step"][s_], (r_key, s_)
+            assert int(st.keep_from[0]) == g["keep_from_by_step"][s_]
+            # the appended rows and their projections are in the caches
+            np.testing.assert_array_equal(st.K[0, ctx - nn:ctx], K[ctx - nn:ctx])
+            np.testing.assert_array_equal(st.Kp[0, ctx - nn:ctx, 0], np.array(scores[ctx - nn:ctx]))
 
 
 def test_interval_one_is_per_step_recompute():
