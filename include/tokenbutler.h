@@ -311,6 +311,26 @@ typedef struct tb_step_args {
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                    const tb_step_args *args, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * tb_decode_step_noalloc -- tb_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is a fixed device array
+ * inside the library (TB_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * library's load until the process ends), so the caller passes only the
+ * step's arguments.  Same computation, kernels and results as
+ * tb_decode_step; no hipMalloc, hipFree or allocating library call is made.
+ * Each call first clears the scratch words that must start at zero with a
+ * small kernel on `stream`.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on
+ * one GPU (other streams, other threads) race and give undefined results.
+ * Errors: as tb_decode_step; TB_EWORKSPACE when tb_workspace_bytes() of the
+ * shape exceeds TB_NOALLOC_SCRATCH_BYTES (nothing is launched);
+ * TB_EHIP if the scratch's device address cannot be obtained.
+ */
+#define TB_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int tb_decode_step_noalloc(const tb_shape *shape, const tb_select_params *params,
+                           const tb_step_args *args, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -2,6 +2,9 @@
 // workspace layout, and the launch sequence of each entry point.
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tb_internal.h"
 
 using namespace tb;
@@ -112,6 +115,121 @@ int check_mlp(const tb_mlp_shape *s)
             return rc_;                                                                            \
     } while (0)
 
+// Clears n words (a kernel rather than a memset, so that graph capture
+// records no memset node).
+__global__ void zero_words_kernel(uint32_t *p, int n)
+{
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int n, hipStream_t st)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(blocks), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+int check_step(const tb_shape *shape, const tb_select_params *params, const tb_step_args *a)
+{
+    TB_TRY(check_shape(shape));
+    TB_TRY(check_params(params));
+    if (a == nullptr)
+        return TB_EINVAL;
+    if (a->q == nullptr || a->w == nullptr || a->k_cache == nullptr || a->v_cache == nullptr ||
+        a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_count == nullptr ||
+        a->sel_bits == nullptr || a->keep_from == nullptr || a->out == nullptr)
+        return TB_EINVAL;
+    if (a->n_new < 0 || (a->n_new > 0 && (a->k_new == nullptr || a->v_new == nullptr)))
+        return TB_EINVAL;
+    if (a->refresh && a->q_imp == nullptr)
+        return TB_EINVAL;
+    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
+        !aligned16(a->kp_cache) || !aligned16(a->w) || !aligned16(a->k_new) ||
+        !aligned16(a->v_new))
+        return TB_EINVAL;
+    if (!(a->softmax_scale == a->softmax_scale))
+        return TB_EINVAL;
+    return TB_OK;
+}
+
+// The launch sequence of one fused step on a checked workspace.
+int decode_step_run(const tb_shape &shape, const tb_select_params &params, const tb_step_args &args,
+                    void *ws, const WsLayout &L, hipStream_t st)
+{
+    const tb_step_args *a = &args;
+    Ws W = carve(ws, L);
+    const int32_t stride = sel_capacity(shape, params);
+
+    // A few new rows are appended inside the score launch (refresh steps) or
+    // the attention launch (reuse steps); more take a launch of their own.
+    const bool fused_append = a->n_new > 0 && a->n_new <= score_max_fused_new();
+    if (a->n_new > 0 && !fused_append)
+        TB_TRY(hip_rc(launch_append_project(shape, a->k_new, a->v_new, a->n_new, a->w,
+                                            a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
+                                            st)));
+    if (a->refresh) {
+        // the 16-bit keys and their sample only where the selection reads them
+        const bool k16 = select_key16(shape.ctx_cap);
+        TB_TRY(hip_rc(launch_score(shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
+                                   fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
+                                   a->k_cache, a->v_cache, k16 ? W.keys16 : nullptr,
+                                   k16 ? W.sample16 : nullptr, st)));
+        TB_TRY(hip_rc(launch_select(shape, params, W.scores, a->ctx_len, a->sel_idx, stride,
+                                    a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
+                                    k16 ? W.keys16 : nullptr, k16 ? W.sample16 : nullptr, st)));
+    }
+    AttnAppend app;
+    if (!a->refresh && fused_append) {
+        app.k_new = a->k_new;
+        app.v_new = a->v_new;
+        app.w = a->w;
+        app.k_cache = a->k_cache;
+        app.v_cache = a->v_cache;
+        app.kp_cache = a->kp_cache;
+        app.n_new = a->n_new;
+    }
+    return hip_rc(launch_attn(shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
+                              a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,
+                              a->softmax_scale, a->out, W.part_o, W.part_ml, W.counters, st,
+                              app));
+}
+
+// ---------------------------------------------------------------- scratch
+// The device memory of tb_decode_step_noalloc: a file-scope array that every
+// device holds from the library's load until the process ends.  In host code
+// the array's name only stands for the symbol; its device address is taken
+// once per device with hipGetSymbolAddress (with that device current) and
+// that address is what the kernels receive.
+__device__ __align__(256) unsigned char scratch[TB_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return TB_EHIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return TB_EUNSUPPORTED;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+                return TB_EHIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return TB_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -124,7 +242,10 @@ const char *tb_strerror(int code)
     case TB_OK: return "ok";
     case TB_EINVAL: return "invalid argument (null pointer, bad size, misaligned pointer or inconsistent head counts)";
     case TB_EUNSUPPORTED: return "unsupported dtype, head_dim, d_imp, group size, ctx_cap, activation or MLP size";
-    case TB_EWORKSPACE: return "workspace smaller than tb_workspace_bytes()";
+    case TB_EWORKSPACE:
+        return "workspace smaller than tb_workspace_bytes() (for tb_decode_step_noalloc: the "
+               "shape needs more than the library's fixed device scratch, "
+               "TB_NOALLOC_SCRATCH_BYTES)";
     case TB_EHIP: return "HIP kernel launch failed";
     }
     return "unknown tokenbutler error code";
@@ -271,63 +392,27 @@ int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1,
 int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
                    const tb_step_args *a, void *ws, size_t ws_bytes, void *stream)
 {
-    TB_TRY(check_shape(shape));
-    TB_TRY(check_params(params));
-    if (a == nullptr)
-        return TB_EINVAL;
-    if (a->q == nullptr || a->w == nullptr || a->k_cache == nullptr || a->v_cache == nullptr ||
-        a->kp_cache == nullptr || a->ctx_len == nullptr || a->sel_count == nullptr ||
-        a->sel_bits == nullptr || a->keep_from == nullptr ||
-        a->out == nullptr)
-        return TB_EINVAL;
-    if (a->n_new < 0 || (a->n_new > 0 && (a->k_new == nullptr || a->v_new == nullptr)))
-        return TB_EINVAL;
-    if (a->refresh && a->q_imp == nullptr)
-        return TB_EINVAL;
-    if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
-        !aligned16(a->kp_cache) || !aligned16(a->w) || !aligned16(a->k_new) ||
-        !aligned16(a->v_new))
-        return TB_EINVAL;
-    if (!(a->softmax_scale == a->softmax_scale))
-        return TB_EINVAL;
+    TB_TRY(check_step(shape, params, a));
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
-    Ws W = carve(ws, L);
-    hipStream_t st = (hipStream_t)stream;
-    const int32_t stride = sel_capacity(*shape, *params);
+    return decode_step_run(*shape, *params, *a, ws, L, (hipStream_t)stream);
+}
 
-    // A few new rows are appended inside the score launch (refresh steps) or
-    // the attention launch (reuse steps); more take a launch of their own.
-    const bool fused_append = a->n_new > 0 && a->n_new <= score_max_fused_new();
-    if (a->n_new > 0 && !fused_append)
-        TB_TRY(hip_rc(launch_append_project(*shape, a->k_new, a->v_new, a->n_new, a->w,
-                                            a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
-                                            st)));
-    if (a->refresh) {
-        // the 16-bit keys and their sample only where the selection reads them
-        const bool k16 = select_key16(shape->ctx_cap);
-        TB_TRY(hip_rc(launch_score(*shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
-                                   fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
-                                   a->k_cache, a->v_cache, k16 ? W.keys16 : nullptr,
-                                   k16 ? W.sample16 : nullptr, st)));
-        TB_TRY(hip_rc(launch_select(*shape, *params, W.scores, a->ctx_len, a->sel_idx, stride,
-                                    a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
-                                    k16 ? W.keys16 : nullptr, k16 ? W.sample16 : nullptr, st)));
-    }
-    AttnAppend app;
-    if (!a->refresh && fused_append) {
-        app.k_new = a->k_new;
-        app.v_new = a->v_new;
-        app.w = a->w;
-        app.k_cache = a->k_cache;
-        app.v_cache = a->v_cache;
-        app.kp_cache = a->kp_cache;
-        app.n_new = a->n_new;
-    }
-    return hip_rc(launch_attn(*shape, a->q, a->k_cache, a->v_cache, a->sel_idx, stride,
-                              a->sel_count, a->sel_bits, a->keep_from, a->ctx_len,
-                              a->softmax_scale, a->out, W.part_o, W.part_ml, W.counters, st,
-                              app));
+int tb_decode_step_noalloc(const tb_shape *shape, const tb_select_params *params,
+                           const tb_step_args *a, void *stream)
+{
+    TB_TRY(check_step(shape, params, a));
+    const WsLayout L = ws_layout(*shape);
+    if (L.total > (size_t)TB_NOALLOC_SCRATCH_BYTES)
+        return TB_EWORKSPACE;
+    void *ws = nullptr;
+    TB_TRY(scratch_of_current_device(&ws));
+    hipStream_t st = (hipStream_t)stream;
+    // the scratch keeps whatever the last call on this device left: the
+    // words that must start at zero are cleared by a kernel (not a memset
+    // node, so that the call can be captured in a graph)
+    TB_TRY(hip_rc(launch_zero_words((uint32_t *)((char *)ws + L.zeroed), L.zeroed_words, st)));
+    return decode_step_run(*shape, *params, *a, ws, L, st);
 }
 
 } // extern "C"

@@ -170,6 +170,8 @@ struct WsLayout {
     size_t keys16;   // top 16 bits of each score's key [b][Himp][keys16_stride] u16,
                      // in pair order (fused step)
     size_t sample16; // the same for positions 8m, compact [b][Himp][sample16_stride] u16
+    size_t zeroed;       // the words that must be zero when a call starts (the
+    int zeroed_words;    //  arrival counters), kept zero by every completed call
     size_t total;
 };
 
@@ -210,6 +212,8 @@ inline WsLayout ws_layout(const tb_shape &s)
     L.part_ml = off;
     off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * 2 * sizeof(float));
     L.counters = off;
+    L.zeroed = off;
+    L.zeroed_words = s.batch * s.n_kv_heads;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
     L.keys16 = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * keys16_stride(s.ctx_cap) *

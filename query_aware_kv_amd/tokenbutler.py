@@ -86,12 +86,14 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_size_t, _vp]
         L.tb_decode_step.argtypes = [P(Shape), P(SelectParams), P(StepArgs), _vp,
                                      ctypes.c_size_t, _vp]
+        L.tb_decode_step_noalloc.argtypes = [P(Shape), P(SelectParams), P(StepArgs), _vp]
         L.tb_mlp_workspace_bytes.argtypes = [P(MlpShape)]
         L.tb_mlp_workspace_bytes.restype = ctypes.c_size_t
         L.tb_predict_queries.argtypes = [P(MlpShape), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                          _vp]
         for fn in ("tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn",
-                   "tb_dense_attn", "tb_decode_step", "tb_predict_queries"):
+                   "tb_dense_attn", "tb_decode_step", "tb_decode_step_noalloc",
+                   "tb_predict_queries"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -346,3 +348,12 @@ def decode_step(shape, params, args: StepArgs, ws, stream=None):
     _check("tb_decode_step", lib().tb_decode_step(
         ctypes.byref(shape), ctypes.byref(params), ctypes.byref(args), _ptr(ws),
         ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TB_NOALLOC_SCRATCH_BYTES
+
+
+def decode_step_noalloc(shape, params, args: StepArgs, stream=None):
+    """tb_decode_step on the library's fixed device scratch (no workspace)."""
+    _check("tb_decode_step_noalloc", lib().tb_decode_step_noalloc(
+        ctypes.byref(shape), ctypes.byref(params), ctypes.byref(args), _stream(stream)))

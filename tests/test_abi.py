@@ -206,3 +206,23 @@ def test_decode_step_argument_checks():
     a.softmax_scale = float("nan")
     assert L.tb_decode_step(ctypes.byref(s), ctypes.byref(p), ctypes.byref(a),
                             ctypes.c_void_p(fake), need, None) == tbl.TB_EINVAL
+
+
+def test_noalloc_step_rejects_a_shape_beyond_its_scratch_on_the_host():
+    # the size check precedes every HIP call: no GPU needed
+    shape = _shape(batch=64)
+    params = tbl.make_params(3277, 0)
+    assert tbl.workspace_bytes(shape, params) > tbl.NOALLOC_SCRATCH_BYTES
+    args = tbl.StepArgs()
+    for f in ("q", "q_imp", "w", "k_cache", "v_cache", "kp_cache", "out", "ctx_len",
+              "sel_count", "sel_bits", "keep_from"):
+        setattr(args, f, 256)
+    args.softmax_scale = 0.1
+    args.refresh = 1
+    rc = tbl.lib().tb_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(params),
+                                          ctypes.byref(args), None)
+    assert rc == tbl.TB_EWORKSPACE
+    # and the shape checks come first
+    bad = _shape(head_dim=96)
+    assert tbl.lib().tb_decode_step_noalloc(ctypes.byref(bad), ctypes.byref(params),
+                                            ctypes.byref(args), None) == tbl.TB_EUNSUPPORTED
