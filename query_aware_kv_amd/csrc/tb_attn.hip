@@ -444,24 +444,6 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
 constexpr int kAttnWindowPairs = 2;
 
 
-// Compute units of the current device, queried once per device.
-hipError_t device_cus(int &cus)
-{
-    static std::atomic<int> known[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    cus = dev < 64 ? known[dev].load(std::memory_order_relaxed) : 0;
-    if (cus > 0)
-        return hipSuccess;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess)
-        return e;
-    if (dev < 64)
-        known[dev].store(cus, std::memory_order_relaxed);
-    return hipSuccess;
-}
 
 template <typename T, int D, int GQ, bool BITMAP, bool APPEND>
 hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
@@ -513,6 +495,25 @@ hipError_t attn_gq(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 }
 
 } // namespace
+
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int &cus)
+{
+    static std::atomic<int> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    cus = dev < 64 ? known[dev].load(std::memory_order_relaxed) : 0;
+    if (cus > 0)
+        return hipSuccess;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 64)
+        known[dev].store(cus, std::memory_order_relaxed);
+    return hipSuccess;
+}
 
 hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
                        const void *v_cache, const int32_t *sel_idx, int sel_stride,

@@ -29,42 +29,26 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f)
     return (bf16_t)(u >> 16);
 }
 
-// fp64 -> bf16, correctly rounded (to nearest even) in one step.  Rounding
-// through fp32 first could round twice, so the 53-bit significand is cut
-// directly: 8 significant bits in the normal range, multiples of 2^-133 below
-// 2^-126.
+// fp64 -> bf16, correctly rounded (to nearest even).  x is first rounded to
+// fp32 with round-to-odd (toward zero, last bit set when inexact), then to
+// bf16 to nearest even: fp32 has 16 more significand bits than bf16 over the
+// same exponent range (subnormals included), so the odd bit carries all a
+// second rounding needs and the two steps round once (Boldo and Melquiond,
+// "When double rounding is odd", 2005).  Needs fp32 subnormals preserved,
+// the default mode of these kernels.
 __device__ __forceinline__ bf16_t f64_to_bf16(double x)
 {
-    uint64_t u = (uint64_t)__double_as_longlong(x);
-    uint32_t sign = (uint32_t)(u >> 63) << 15;
-    int ex = (int)((u >> 52) & 0x7ff);
-    uint64_t man = u & 0xFFFFFFFFFFFFFull;
-    if (ex == 0x7ff)
-        return (bf16_t)(sign | 0x7f80u | (man ? 0x40u : 0u));
-    if (ex == 0)
-        return (bf16_t)sign; // fp64 zero / subnormal: far below bf16's range
-    int e = ex - 1023;
-    if (e > 127)
-        return (bf16_t)(sign | 0x7f80u);
-    int shift = e >= -126 ? 45 : -81 - e;
-    if (shift > 60)
-        return (bf16_t)sign;
-    uint64_t full = man | (1ull << 52);
-    uint64_t keep = full >> shift;
-    uint64_t rem = full & ((1ull << shift) - 1);
-    uint64_t half = 1ull << (shift - 1);
-    if (rem > half || (rem == half && (keep & 1)))
-        keep += 1;
-    if (e >= -126) {
-        if (keep == 256) {
-            keep = 128;
-            e += 1;
-            if (e > 127)
-                return (bf16_t)(sign | 0x7f80u);
-        }
-        return (bf16_t)(sign | ((uint32_t)(e + 127) << 7) | (uint32_t)(keep & 0x7f));
+    if (x != x)
+        return (bf16_t)(((uint32_t)((uint64_t)__double_as_longlong(x) >> 48) & 0x8000u) | 0x7fc0u);
+    const float f = (float)x; // to nearest even
+    const double back = (double)f;
+    uint32_t u = __float_as_uint(f);
+    if (back != x) {
+        if (fabs(back) > fabs(x))
+            u -= 1u; // one step toward zero (infinity becomes the largest finite)
+        u |= 1u;
     }
-    return (bf16_t)(sign | (uint32_t)keep); // keep == 128 encodes 2^-126
+    return f32_to_bf16(__uint_as_float(u));
 }
 
 template <typename T> __device__ __forceinline__ T from_f64(double x);
@@ -99,6 +83,16 @@ __device__ __forceinline__ void lds_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0); vmcnt and expcnt untouched
     __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The same for the lanes of one wave: the wave's LDS operations have
+// completed, so other lanes of the wave read what it wrote.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
@@ -226,6 +220,9 @@ inline WsLayout ws_layout(const tb_shape &s)
 }
 
 // ---------------------------------------------------------------- launchers
+// Compute units of the current device, queried once per device.
+hipError_t device_cus(int &cus);
+
 // Each returns hipSuccess or the launch error.  Shapes are already validated.
 hipError_t launch_project(const tb_shape &s, const void *k_cache, const void *w,
                           const int32_t *pos0, int n_tokens, void *kp_cache, hipStream_t st);

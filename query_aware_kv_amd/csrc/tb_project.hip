@@ -10,11 +10,12 @@
 // Precision contract: kp = round_to_dtype( sum_{i ascending} k[i] * W[i][j] )
 // with the sum in fp64.  Every product of two bf16 (or two fp32) values is
 // exact in fp64, so a fused multiply-add in ascending i yields the same bits
-// as the plain fp64 sum; the result is rounded once.  MI355X runs fp64 FMA at
-// the same vector rate as non-packed fp32, and fp64 MFMA has the same peak,
-// so the dense contraction stays on the vector ALU where its summation order
-// is fixed.
+// as the plain fp64 sum; the result is rounded once.  Small batches use the
+// vector ALU; prefill-sized batches use the fp64 matrix cores, whose
+// 16x16x4 instruction keeps the same order and rounding (see below).
 #include "tb_internal.h"
+
+#include <atomic>
 
 namespace tb {
 namespace {
@@ -100,94 +101,166 @@ __global__ __launch_bounds__(256) void project_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Many rows (prefill-sized batches): each thread owns RPT rows x OPT output
-// columns, so every W value read from LDS feeds RPT fma and every K value
-// feeds OPT fma.  K rows stream from HBM in 16-byte pieces.
+// Many rows (prefill-sized batches): the dense contraction on the fp64 matrix
+// cores.  v_mfma_f64_16x16x4f64 adds its four products to the accumulator one
+// after another in k order, rounding after each addition (crafted inputs
+// whose fp64 sum depends on the order give the sequential result); the
+// products here are exact in fp64, so a chain of these instructions over
+// head_dim in ascending order is the fp64 chain of the precision contract.
+//
+// Operand layout of the instruction: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] and holds D[l / 16 + 4 v][l % 16] in its v-th double.
+// Here A is 16 key rows x 4 head_dim values, B the matching 4 rows of W.
+// A work-group of 4 waves loops over blocks of rows; each wave owns 16 rows
+// (32 when d = 16, so that two independent accumulators alternate) and all d
+// outputs.  W stays in registers for the whole launch: lane l holds
+// W[4 s + l / 16][16 n + l % 16] for every head_dim step s and output tile n.
+// A block of keys is read with consecutive lanes on consecutive 16-byte
+// pieces of whole rows (coalesced, every byte once), the next block in flight
+// while the current one is multiplied, and stored in LDS as [row][i % 4][i / 4]
+// so that a lane's A operands for 8 (bf16) or 4 (fp32) consecutive steps are
+// one 16-byte read.  Results pass through a per-wave LDS tile to 16-byte
+// stores of whole output rows.
 // ---------------------------------------------------------------------------
+constexpr int kWideThreads = 256;
+
+template <int DI> struct WideTile {
+    static constexpr int NT = DI / 16;         // output tiles of 16
+    static constexpr int RT = NT >= 2 ? 1 : 2; // row tiles of 16 per wave
+    static constexpr int WROWS = 16 * RT;      // rows per wave
+    static constexpr int BROWS = 4 * WROWS;    // rows per block
+};
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <typename T, int D, int DI>
-__global__ __launch_bounds__(256) void project_wide_kernel(
+__global__ __launch_bounds__(kWideThreads) void project_wide_kernel(
     const T *__restrict__ k_cache, const T *__restrict__ w, const int32_t *__restrict__ pos0,
-    int n_tokens, int Hkv, int cap, int rows_total, T *__restrict__ kp)
+    int n_tokens, int Hkv, int cap, int rows_total, int n_blocks, T *__restrict__ kp)
 {
-    constexpr int OPT = 8;
-    constexpr int RPT = 4;
-    constexpr int JS = DI / OPT;
-    constexpr int RG = 256 / JS;
-    constexpr int ROWS = RG * RPT;
-    constexpr int EPC = 16 / sizeof(T); // elements per 16-byte piece
-    __shared__ double sW[D * DI];
+    using Tile = WideTile<DI>;
+    constexpr int NT = Tile::NT, RT = Tile::RT, WROWS = Tile::WROWS, BROWS = Tile::BROWS;
+    constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte piece
+    constexpr int CPR = D / EPC;                    // pieces per key row
+    constexpr int CPT = BROWS * CPR / kWideThreads; // pieces per thread and block
+    static_assert(CPT * kWideThreads == BROWS * CPR, "whole pieces per thread");
+    constexpr int S = D / 4;                        // head_dim steps of 4
+    constexpr int GRPB = S * (int)sizeof(T);        // bytes of one i % 4 group
+    constexpr int ROWB = 4 * GRPB + 16;             // bytes of one staged row (padded)
+    constexpr int OB = DI * (int)sizeof(T);         // bytes of one output row
+    constexpr int OPR = OB / 16;                    // 16-byte pieces per output row
+    constexpr int OPL = WROWS * OPR / 64;           // output pieces per lane
+    static_assert(OPL * 64 == WROWS * OPR, "whole output pieces per lane");
+    __shared__ __align__(16) unsigned char sK[2][BROWS * ROWB];
+    __shared__ __align__(16) unsigned char sO[4][WROWS * OB];
 
-    stage_w_f64<T, D, DI>(w, sW);
-    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lk = lane >> 4;
 
-    const int js = threadIdx.x % JS;
-    const int rg = threadIdx.x / JS;
-    size_t rowoff[RPT];
-    bool valid[RPT];
+    // cache row of block row r, or -1 (past the end, or outside [0, cap))
+    auto cache_row = [&](int row) -> long long {
+        if (row >= rows_total)
+            return -1;
+        const int bg = row / n_tokens, jj = row - bg * n_tokens;
+        const int t = pos0[bg / Hkv] + jj;
+        if (t < 0 || t >= cap)
+            return -1;
+        return (long long)bg * cap + t;
+    };
+    // piece p = tid + q * threads of a block is piece p % CPR of block row
+    // p / CPR; rows that are not stored read row 0
+    uint4 pc[CPT];
+    auto load_block = [&](int blk) {
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-        const int row = blockIdx.x * ROWS + rg + RG * rr;
-        valid[rr] = false;
-        rowoff[rr] = 0;
-        if (row < rows_total) {
-            const int bg = row / n_tokens;
-            const int jj = row - bg * n_tokens;
-            const int t = pos0[bg / Hkv] + jj;
-            if (t >= 0 && t < cap) {
-                valid[rr] = true;
-                rowoff[rr] = (size_t)bg * cap + t;
+        for (int q = 0; q < CPT; ++q) {
+            const int p = threadIdx.x + q * kWideThreads;
+            const long long cr = cache_row(blk * BROWS + p / CPR);
+            pc[q] = *reinterpret_cast<const uint4 *>(k_cache + (size_t)(cr < 0 ? 0 : cr) * D +
+                                                     (size_t)(p % CPR) * EPC);
+        }
+    };
+    if ((int)blockIdx.x < n_blocks)
+        load_block(blockIdx.x);
+
+    double wr[S][NT];
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            wr[st][n] = to_f64(w[(4 * st + lk) * DI + 16 * n + lr]);
+
+    int it = 0;
+    for (int blk = blockIdx.x; blk < n_blocks; blk += gridDim.x, ++it) {
+        unsigned char *buf = sK[it & 1];
+        // element i of a row goes to [i % 4][i / 4]
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int p = threadIdx.x + q * kWideThreads;
+            unsigned char *row = buf + (p / CPR) * ROWB;
+            const int c = p % CPR;
+            if constexpr (EPC == 8) { // elements e and e + 4 are neighbours in group e
+                const uint32_t x[4] = {pc[q].x, pc[q].y, pc[q].z, pc[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                    const uint32_t hi = (x[2 + (e >> 1)] >> (16 * (e & 1))) & 0xffffu;
+                    *reinterpret_cast<uint32_t *>(row + e * GRPB + c * 4) = lo | (hi << 16);
+                }
+            } else {
+                const uint32_t x[4] = {pc[q].x, pc[q].y, pc[q].z, pc[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<uint32_t *>(row + e * GRPB + c * 4) = x[e];
             }
         }
-    }
+        __syncthreads(); // this block staged; the other buffer is free again
+        if (blk + (int)gridDim.x < n_blocks)
+            load_block(blk + gridDim.x);
 
-    double acc[RPT][OPT];
+        f64x4 acc[RT][NT];
 #pragma unroll
-    for (int rr = 0; rr < RPT; ++rr)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int o = 0; o < OPT; ++o)
-            acc[rr][o] = 0.0;
-
-    for (int i0 = 0; i0 < D; i0 += EPC) {
-        T kv[RPT][EPC];
+            for (int n = 0; n < NT; ++n)
+                acc[rt][n] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int rr = 0; rr < RPT; ++rr) {
-            // unconditional (an invalid row reads row 0 and is not stored), so
-            // the loads issue back to back
-            const uint4 piece = *reinterpret_cast<const uint4 *>(k_cache + rowoff[rr] * D + i0);
-            __builtin_memcpy(kv[rr], &piece, 16);
+        for (int q = 0; q < S / EPC; ++q) {
+            T av[RT][EPC];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                __builtin_memcpy(av[rt], buf + (wave * WROWS + rt * 16 + lr) * ROWB + lk * GRPB + q * 16,
+                                 16);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const double a = to_f64(av[rt][e]);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc[rt][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, wr[q * EPC + e][n],
+                                                                          acc[rt][n], 0, 0, 0);
+                }
         }
+        // outputs to the wave's LDS tile, then whole rows to the cache
+        unsigned char *ot = sO[wave];
 #pragma unroll
-        for (int ii = 0; ii < EPC; ++ii) {
-            const double2 *wp = reinterpret_cast<const double2 *>(&sW[(i0 + ii) * DI + js * OPT]);
-            double wv[OPT];
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int o2 = 0; o2 < OPT / 2; ++o2) {
-                const double2 p = wp[o2];
-                wv[2 * o2] = p.x;
-                wv[2 * o2 + 1] = p.y;
-            }
+            for (int n = 0; n < NT; ++n)
 #pragma unroll
-            for (int rr = 0; rr < RPT; ++rr) {
-                const double k = to_f64(kv[rr][ii]);
+                for (int v = 0; v < 4; ++v)
+                    *reinterpret_cast<T *>(ot + (rt * 16 + lk + 4 * v) * OB +
+                                           (16 * n + lr) * (int)sizeof(T)) = from_f64<T>(acc[rt][n][v]);
+        wave_lds_sync();
 #pragma unroll
-                for (int o = 0; o < OPT; ++o)
-                    acc[rr][o] = fma(k, wv[o], acc[rr][o]);
-            }
+        for (int u = 0; u < OPL; ++u) {
+            const int pi = lane + 64 * u, r = pi / OPR;
+            const uint4 val = *reinterpret_cast<const uint4 *>(ot + pi * 16);
+            const long long cr = cache_row(blk * BROWS + wave * WROWS + r);
+            if (cr >= 0)
+                *reinterpret_cast<uint4 *>(kp + (size_t)cr * DI + (pi % OPR) * (16 / (int)sizeof(T))) = val;
         }
-    }
-
-#pragma unroll
-    for (int rr = 0; rr < RPT; ++rr) {
-        if (!valid[rr])
-            continue;
-        T res[OPT];
-#pragma unroll
-        for (int o = 0; o < OPT; ++o)
-            res[o] = from_f64<T>(acc[rr][o]);
-        T *dst = kp + rowoff[rr] * DI + js * OPT;
-#pragma unroll
-        for (int p = 0; p < OPT * (int)sizeof(T) / 16; ++p)
-            reinterpret_cast<uint4 *>(dst)[p] = reinterpret_cast<const uint4 *>(res)[p];
+        wave_lds_sync(); // the tile is read before the next block writes it
     }
 }
 
@@ -197,11 +270,26 @@ hipError_t project_dispatch_t(const tb_shape &s, const void *k_cache, const void
 {
     const long rows = (long)s.batch * s.n_kv_heads * n;
     if (rows >= 16384) {
-        constexpr int ROWS = (256 / (DI / 8)) * 4;
-        const int grid = (int)((rows + ROWS - 1) / ROWS);
-        hipLaunchKernelGGL((project_wide_kernel<T, D, DI>), dim3(grid), dim3(256), 0, st,
+        // persistent work-groups: as many as fit on the device at once
+        static std::atomic<int> per_cu{0};
+        int fit = per_cu.load(std::memory_order_relaxed);
+        if (fit <= 0) {
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &fit, reinterpret_cast<const void *>(&project_wide_kernel<T, D, DI>), kWideThreads, 0);
+            if (e != hipSuccess)
+                return e;
+            fit = fit < 1 ? 1 : fit;
+            per_cu.store(fit, std::memory_order_relaxed);
+        }
+        int cus = 0;
+        const hipError_t e = device_cus(cus);
+        if (e != hipSuccess)
+            return e;
+        const int n_blocks = (int)((rows + WideTile<DI>::BROWS - 1) / WideTile<DI>::BROWS);
+        const int grid = n_blocks < fit * cus ? n_blocks : fit * cus;
+        hipLaunchKernelGGL((project_wide_kernel<T, D, DI>), dim3(grid), dim3(kWideThreads), 0, st,
                            (const T *)k_cache, (const T *)w, pos0, n, s.n_kv_heads, s.ctx_cap,
-                           (int)rows, (T *)kp);
+                           (int)rows, n_blocks, (T *)kp);
     } else {
         constexpr int ROWS = 256 / DI;
         const int grid = (int)((rows + ROWS - 1) / ROWS);
