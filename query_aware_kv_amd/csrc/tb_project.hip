@@ -123,9 +123,10 @@ __global__ __launch_bounds__(256) void project_rows_kernel(
 // stores of whole output rows.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
+constexpr int kWidePosLds = 256; // sequences whose pos0 is kept in LDS
 
-template <int DI> struct WideTile {
-    static constexpr int NT = DI / 16;         // output tiles of 16
+template <typename T, int DI> struct WideTile {
+    static constexpr int NT = DI / 16; // output tiles of 16
     static constexpr int RT = NT >= 2 ? 1 : 2; // row tiles of 16 per wave
     static constexpr int WROWS = 16 * RT;      // rows per wave
     static constexpr int BROWS = 4 * WROWS;    // rows per block
@@ -136,9 +137,9 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 template <typename T, int D, int DI>
 __global__ __launch_bounds__(kWideThreads) void project_wide_kernel(
     const T *__restrict__ k_cache, const T *__restrict__ w, const int32_t *__restrict__ pos0,
-    int n_tokens, int Hkv, int cap, int rows_total, int n_blocks, T *__restrict__ kp)
+    int batch, int n_tokens, int Hkv, int cap, int rows_total, int n_blocks, T *__restrict__ kp)
 {
-    using Tile = WideTile<DI>;
+    using Tile = WideTile<T, DI>;
     constexpr int NT = Tile::NT, RT = Tile::RT, WROWS = Tile::WROWS, BROWS = Tile::BROWS;
     constexpr int EPC = 16 / (int)sizeof(T);        // elements per 16-byte piece
     constexpr int CPR = D / EPC;                    // pieces per key row
@@ -153,30 +154,56 @@ __global__ __launch_bounds__(kWideThreads) void project_wide_kernel(
     static_assert(OPL * 64 == WROWS * OPR, "whole output pieces per lane");
     __shared__ __align__(16) unsigned char sK[2][BROWS * ROWB];
     __shared__ __align__(16) unsigned char sO[4][WROWS * OB];
+    __shared__ int32_t sPos[kWidePosLds];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lk = lane >> 4;
 
-    // cache row of block row r, or -1 (past the end, or outside [0, cap))
-    auto cache_row = [&](int row) -> long long {
+    for (int i = threadIdx.x; i < batch && i < kWidePosLds; i += kWideThreads)
+        sPos[i] = pos0[i];
+    __syncthreads();
+    // row = (b Hkv + g) n_tokens + jj: one division pair per run of rows,
+    // then steps along the run
+    struct RowAt {
+        int b, g, jj;
+    };
+    auto row_at = [&](int row) {
+        const int bg = row / n_tokens, b = bg / Hkv;
+        return RowAt{b, bg - b * Hkv, row - bg * n_tokens};
+    };
+    auto advance = [&](RowAt &r, int k) {
+        r.jj += k;
+        while (r.jj >= n_tokens) {
+            r.jj -= n_tokens;
+            if (++r.g == Hkv) {
+                r.g = 0;
+                ++r.b;
+            }
+        }
+    };
+    // cache row, or -1 (past the last row, or t outside [0, cap))
+    auto cache_of = [&](int row, const RowAt &r) -> long long {
         if (row >= rows_total)
             return -1;
-        const int bg = row / n_tokens, jj = row - bg * n_tokens;
-        const int t = pos0[bg / Hkv] + jj;
+        const int t = (r.b < kWidePosLds ? sPos[r.b] : pos0[r.b]) + r.jj;
         if (t < 0 || t >= cap)
             return -1;
-        return (long long)bg * cap + t;
+        return ((long long)r.b * Hkv + r.g) * cap + t;
     };
     // piece p = tid + q * threads of a block is piece p % CPR of block row
     // p / CPR; rows that are not stored read row 0
+    constexpr int QS = kWideThreads / CPR; // block rows between a thread's pieces
     uint4 pc[CPT];
     auto load_block = [&](int blk) {
+        const int row0 = blk * BROWS + (int)threadIdx.x / CPR;
+        RowAt at = row_at(row0);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
-            const int p = threadIdx.x + q * kWideThreads;
-            const long long cr = cache_row(blk * BROWS + p / CPR);
+            const long long cr = cache_of(row0 + q * QS, at);
             pc[q] = *reinterpret_cast<const uint4 *>(k_cache + (size_t)(cr < 0 ? 0 : cr) * D +
-                                                     (size_t)(p % CPR) * EPC);
+                                                     (size_t)(threadIdx.x % CPR) * EPC);
+            if (q + 1 < CPT)
+                advance(at, QS);
         }
     };
     if ((int)blockIdx.x < n_blocks)
@@ -252,13 +279,19 @@ __global__ __launch_bounds__(kWideThreads) void project_wide_kernel(
                     *reinterpret_cast<T *>(ot + (rt * 16 + lk + 4 * v) * OB +
                                            (16 * n + lr) * (int)sizeof(T)) = from_f64<T>(acc[rt][n][v]);
         wave_lds_sync();
+        {
+            const int row0 = blk * BROWS + wave * WROWS + lane / OPR;
+            RowAt at = row_at(row0);
 #pragma unroll
-        for (int u = 0; u < OPL; ++u) {
-            const int pi = lane + 64 * u, r = pi / OPR;
-            const uint4 val = *reinterpret_cast<const uint4 *>(ot + pi * 16);
-            const long long cr = cache_row(blk * BROWS + wave * WROWS + r);
-            if (cr >= 0)
-                *reinterpret_cast<uint4 *>(kp + (size_t)cr * DI + (pi % OPR) * (16 / (int)sizeof(T))) = val;
+            for (int u = 0; u < OPL; ++u) {
+                const int pi = lane + 64 * u;
+                const uint4 val = *reinterpret_cast<const uint4 *>(ot + pi * 16);
+                const long long cr = cache_of(row0 + u * (64 / OPR), at);
+                if (cr >= 0)
+                    *reinterpret_cast<uint4 *>(kp + (size_t)cr * DI + (pi % OPR) * (16 / (int)sizeof(T))) = val;
+                if (u + 1 < OPL)
+                    advance(at, 64 / OPR);
+            }
         }
         wave_lds_sync(); // the tile is read before the next block writes it
     }
@@ -285,11 +318,11 @@ hipError_t project_dispatch_t(const tb_shape &s, const void *k_cache, const void
         const hipError_t e = device_cus(cus);
         if (e != hipSuccess)
             return e;
-        const int n_blocks = (int)((rows + WideTile<DI>::BROWS - 1) / WideTile<DI>::BROWS);
+        const int n_blocks = (int)((rows + WideTile<T, DI>::BROWS - 1) / WideTile<T, DI>::BROWS);
         const int grid = n_blocks < fit * cus ? n_blocks : fit * cus;
         hipLaunchKernelGGL((project_wide_kernel<T, D, DI>), dim3(grid), dim3(kWideThreads), 0, st,
-                           (const T *)k_cache, (const T *)w, pos0, n, s.n_kv_heads, s.ctx_cap,
-                           (int)rows, n_blocks, (T *)kp);
+                           (const T *)k_cache, (const T *)w, pos0, s.batch, n, s.n_kv_heads,
+                           s.ctx_cap, (int)rows, n_blocks, (T *)kp);
     } else {
         constexpr int ROWS = 256 / DI;
         const int grid = (int)((rows + ROWS - 1) / ROWS);
