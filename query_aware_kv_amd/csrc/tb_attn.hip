@@ -52,7 +52,9 @@ namespace {
 
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kRowsInFlight = 4; // rows per row slot loaded before use
+// rows per row slot loaded before use: 4 where the windowed walk keeps eight
+// waves per SIMD (64 registers), 8 where a work-group has its unit alone
+template <int WIN> constexpr int rows_in_flight() { return WIN > 0 ? 4 : 8; }
 
 // First index e in [0, cnt] with L[e] >= v for an ascending list, found by
 // one wave; every lane returns the answer.
@@ -161,6 +163,7 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
     constexpr int LPR = D / EPL;             // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave step
     constexpr int NWD = kAttnChunk / 32;     // bitmap words per head
+    constexpr int RIF = rows_in_flight<WIN>();
     static_assert(GQ <= kAttnWaves && kAttnWaves % GQ == 0, "whole waves per query head");
     constexpr int WPH = kAttnWaves / GQ;     // waves per query head
     constexpr int PW = kAttnChunk / WPH;     // positions of one wave's part of the chunk
@@ -333,7 +336,7 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
             vnb = (const T *)a.v_new + src0 * D + sub * EPL;
         }
 
-        // All of a slot's rows (up to kRowsInFlight) are requested before any
+        // All of a slot's rows (up to RIF) are requested before any
         // is used.  The loads are unconditional -- a missing row reads the
         // chunk's first position, which always exists, and is given weight
         // 0 -- so they issue back to back.
@@ -342,18 +345,18 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
         for (int wi = 0; wi < NWIN; ++wi) {
             const uint32_t hi =
                 WIN > 0 ? __builtin_amdgcn_readfirstlane((uint32_t)wend[wave][wi]) : nh;
-            for (uint32_t base = lo + slot; base < hi; base += kRowsInFlight * RPW) {
-                uint32_t pos[kRowsInFlight];
-                bool ok[kRowsInFlight];
-                uint4 kk[kRowsInFlight], vv[kRowsInFlight];
+            for (uint32_t base = lo + slot; base < hi; base += RIF * RPW) {
+                uint32_t pos[RIF];
+                bool ok[RIF];
+                uint4 kk[RIF], vv[RIF];
 #pragma unroll
-                for (int r = 0; r < kRowsInFlight; ++r) {
+                for (int r = 0; r < RIF; ++r) {
                     const uint32_t u = base + r * RPW;
                     ok[r] = u < hi;
                     pos[r] = gpos(ok[r] ? hlist[wave][u] : 0u);
                 }
 #pragma unroll
-                for (int r = 0; r < kRowsInFlight; ++r) {
+                for (int r = 0; r < RIF; ++r) {
                     const T *kr = kb + (size_t)pos[r] * D, *vr = vb + (size_t)pos[r] * D;
                     if constexpr (APPEND)
                         if (pos[r] >= (uint32_t)t_new) {
@@ -364,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
                     vv[r] = *reinterpret_cast<const uint4 *>(vr);
                 }
 #pragma unroll
-                for (int r = 0; r < kRowsInFlight; ++r) {
+                for (int r = 0; r < RIF; ++r) {
                     // logit in base 2, reduced over the row's lanes
                     const float z = group_sum<LPR>(lane_dot<T>(qh, kk[r])) * a.qscale;
                     if (ok[r]) {
