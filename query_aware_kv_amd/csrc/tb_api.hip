@@ -171,15 +171,14 @@ int decode_step_run(const tb_shape &shape, const tb_select_params &params, const
                                             a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
                                             st)));
     if (a->refresh) {
-        // the 16-bit keys and their sample only where the selection reads them
-        const bool k16 = select_key16(shape.ctx_cap);
+        // the score launch also stores the 16-bit keys and their sample,
+        // from which the selection classifies positions
         TB_TRY(hip_rc(launch_score(shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
                                    fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
-                                   a->k_cache, a->v_cache, k16 ? W.keys16 : nullptr,
-                                   k16 ? W.sample16 : nullptr, st)));
+                                   a->k_cache, a->v_cache, W.keys16, W.sample16, st)));
         TB_TRY(hip_rc(launch_select(shape, params, W.scores, a->ctx_len, a->sel_idx, stride,
                                     a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
-                                    k16 ? W.keys16 : nullptr, k16 ? W.sample16 : nullptr, st)));
+                                    W.keys16, W.sample16, st)));
     }
     AttnAppend app;
     if (!a->refresh && fused_append) {

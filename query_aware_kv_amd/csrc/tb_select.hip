@@ -288,7 +288,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     int n_sink, int n_local, const uint16_t *__restrict__ keys16,
     const uint16_t *__restrict__ sample16, int s16)
 {
-    static_assert(!K16 || WPT == 1, "16-bit first pass: one word per thread");
+    static_assert(!K16 || WPT <= 1, "16-bit first pass: one word per thread, or words re-read");
     static_assert(THREADS == 1024 || (THREADS == 512 && K16), "1024 threads, or 512 on rows of <= 512 words");
     constexpr int NWAVES = THREADS / 64;
     extern __shared__ __align__(16) uint32_t lds[];
@@ -318,20 +318,26 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     // again.
     uint2 s16v = make_uint2(0u, 0u);
     uint4 k16v[4] = {};
-    if constexpr (K16) {
-        const int ms = 4 * tid < s16 ? 4 * tid : s16 - 4;
-        s16v = *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + ms);
-        const int wl = (cap + 31) / 32 - 1; // the row's last word
+    // 16-bit keys of whole word w (64 bytes, pair order), and its sample pair
+    const int wlast = (cap + 31) / 32 - 1; // the row's last word
+    auto k16_word = [&](int w, uint4 (&kv)[4]) {
         const uint4 *src = reinterpret_cast<const uint4 *>(
-            keys16 + rowid * (size_t)(32 * (wl + 1)) + 32 * (tid < wl ? tid : wl));
+            keys16 + rowid * (size_t)(32 * (wlast + 1)) + 32 * (w < wlast ? w : wlast));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            k16v[q] = src[q];
-        // A use on a path never taken (the budget is never negative) keeps
-        // these requests ahead of the first branch; otherwise they would
-        // be moved below the early exit, after the context length arrives.
-        if (B < 0)
-            sel_count[rowid] = (int32_t)(s16v.x ^ k16v[0].x ^ k16v[1].x ^ k16v[2].x ^ k16v[3].x);
+            kv[q] = src[q];
+    };
+    auto s16_word = [&](int w) {
+        const int ms = 4 * w < s16 ? 4 * w : s16 - 4;
+        return *reinterpret_cast<const uint2 *>(sample16 + rowid * s16 + ms);
+    };
+    if constexpr (K16 && WPT == 1) {
+        s16v = s16_word(tid);
+        k16_word(tid, k16v);
+        // Nothing is scheduled across this point: the requests stay ahead of
+        // the early exit instead of being moved below it, after the context
+        // length arrives.
+        __builtin_amdgcn_sched_barrier(0);
     }
     // LDS that starts at zero (radix and sample histograms, misc words),
     // cleared before anything depends on the context length
@@ -439,13 +445,15 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
             // (keys 0, 8, 16, 24 of every word), binned by their top 12 bits
             auto sample_word = [&](int j, uint32_t (&s4)[4]) {
                 if constexpr (K16) {
-                    // the 16-bit keys of positions 8(4 tid + q), as the top
-                    // half of a key (enough for the 12-bit sample bins)
-                    (void)j;
-                    const uint32_t pair[2] = {s16v.x, s16v.y};
+                    // the 16-bit keys of positions 8(4 w + q) of this
+                    // thread's word w, as the top half of a key (enough for
+                    // the 12-bit sample bins)
+                    const int w = tid + j * THREADS;
+                    const uint2 sv = WPT == 1 ? s16v : s16_word(w);
+                    const uint32_t pair[2] = {sv.x, sv.y};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int p = 8 * (4 * tid + q);
+                        const int p = 8 * (4 * w + q);
                         const uint32_t k16 = (pair[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
                         s4[q] = p < n && p >= lo && p < hi ? k16 << 16 : 0u;
                     }
@@ -535,31 +543,47 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
                 }
             };
             if constexpr (K16) {
-                // this thread's word from its 16 key pairs (pair j: the
-                // 16-bit keys of positions 32 tid + j and 32 tid + 16 + j),
-                // two keys per packed op: a key's 12-bit bin is key16 >> 4,
-                // so bin > b_hi is key16 >= kt and bin < b_lo is key16 < kl.
-                // sat(kt - key16) is nonzero iff the key is not above the
-                // range, sat(kl - key16) iff it is below; min(., 1) turns
-                // each into the word's bit j (low half) or 16 + j (high half).
-                const uint32_t kw[16] = {k16v[0].x, k16v[0].y, k16v[0].z, k16v[0].w,
-                                         k16v[1].x, k16v[1].y, k16v[1].z, k16v[1].w,
-                                         k16v[2].x, k16v[2].y, k16v[2].z, k16v[2].w,
-                                         k16v[3].x, k16v[3].y, k16v[3].z, k16v[3].w};
+                // a word from its 16 key pairs (pair j: the 16-bit keys of
+                // positions 32 w + j and 32 w + 16 + j), two keys per packed
+                // op: a key's 12-bit bin is key16 >> 4, so bin > b_hi is
+                // key16 >= kt and bin < b_lo is key16 < kl.  sat(kt - key16)
+                // is nonzero iff the key is not above the range,
+                // sat(kl - key16) iff it is below; min(., 1) turns each into
+                // the word's bit j (low half) or 16 + j (high half).
                 const uint32_t kt = b_hi + 1u < 4096u ? (b_hi + 1u) << 4 : 0xFFFFu;
                 const uint32_t ktv = kt * 0x10001u, klv = (b_lo << 4) * 0x10001u;
-                uint32_t not_above = 0u, below = 0u;
+                auto classify = [&](int w, const uint4 (&kv)[4]) {
+                    const uint32_t kw[16] = {kv[0].x, kv[0].y, kv[0].z, kv[0].w,
+                                             kv[1].x, kv[1].y, kv[1].z, kv[1].w,
+                                             kv[2].x, kv[2].y, kv[2].z, kv[2].w,
+                                             kv[3].x, kv[3].y, kv[3].z, kv[3].w};
+                    uint32_t not_above = 0u, below = 0u;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    not_above |= pk_min_u16(pk_sub_sat_u16(ktv, kw[j]), 0x10001u) << j;
-                    below |= pk_min_u16(pk_sub_sat_u16(klv, kw[j]), 0x10001u) << j;
+                    for (int j = 0; j < 16; ++j) {
+                        not_above |= pk_min_u16(pk_sub_sat_u16(ktv, kw[j]), 0x10001u) << j;
+                        below |= pk_min_u16(pk_sub_sat_u16(klv, kw[j]), 0x10001u) << j;
+                    }
+                    // valid: positions of the middle region [lo, hi)
+                    const uint32_t vm = mask_below(w, hi) & ~mask_below(w, lo);
+                    // (with b_hi the top bin no key is above the range)
+                    const uint32_t wt = b_hi + 1u < 4096u ? ~not_above & vm : 0u;
+                    const uint32_t wc = not_above & ~below & vm;
+                    pass_word(w, wt, wc);
+                };
+                if constexpr (WPT == 1) {
+                    classify(tid, k16v);
+                } else {
+                    // longer rows: the words' keys are read here, two words
+                    // in flight at a time
+                    for (int j = 0; j < nwt; j += 2) {
+                        uint4 ka[4], kb[4];
+                        k16_word(tid + j * THREADS, ka);
+                        k16_word(tid + (j + 1) * THREADS, kb);
+                        classify(tid + j * THREADS, ka);
+                        if (j + 1 < nwt)
+                            classify(tid + (j + 1) * THREADS, kb);
+                    }
                 }
-                // valid: positions of the middle region [lo, hi)
-                const uint32_t vm = mask_below(tid, hi) & ~mask_below(tid, lo);
-                // (with b_hi the top bin no key is above the range)
-                const uint32_t wt = b_hi + 1u < 4096u ? ~not_above & vm : 0u;
-                const uint32_t wc = not_above & ~below & vm;
-                pass_word(tid, wt, wc);
             } else {
                 for_words([&](int w, const auto &k) {
                     uint32_t wt = 0u, wc = 0u;
@@ -940,15 +964,16 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
     static_assert(kSelThreads == 1024, "select_key16: one word per thread up to 1024 words");
     static_assert(kSelShortCap / 32 <= 512 && kSelShortCap / 8 <= 4 * 512,
                   "short rows: one word and four sample keys per thread of 512");
+    const bool k16 = keys16 != nullptr && sample16 != nullptr;
     if (select_key16(s.ctx_cap)) {
-        if (keys16 != nullptr && sample16 != nullptr) {
+        if (k16) {
             if (s.ctx_cap <= kSelShortCap)
                 return select_t<1, true, 512>(TB_SEL_ARGS);
             return select_t<1, true, 1024>(TB_SEL_ARGS);
         }
         return select_t<1, false, 1024>(TB_SEL_ARGS);
     }
-    return select_t<0, false, 1024>(TB_SEL_ARGS);
+    return k16 ? select_t<0, true, 1024>(TB_SEL_ARGS) : select_t<0, false, 1024>(TB_SEL_ARGS);
 #undef TB_SEL_ARGS
 }
 

@@ -189,6 +189,26 @@ def test_fused_step_selection_block_sizes(ctx0):
         _check_step(w, dc, oracle_state(w, dc.pre, b), inp, out, 0, b, w.ctx)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(ctx0=32768, batch=2, budget=2000, radius=1),                   # 1025 words
+    dict(ctx0=70000, batch=1, budget=3500, radius=0, n_sink=5, n_local=64,
+         plant_per_head=0, plant_runs=6, plant_run_len=32),             # 2188 words, odd cap
+    dict(ctx0=40000, batch=1, budget=1, radius=2),                      # a budget of one
+], ids=["cap32769", "cap70001_sink_local_runs", "cap40001_budget1"])
+def test_fused_step_long_rows_16bit_keys(kw):
+    # rows longer than 1024 words: the selection classifies each thread's
+    # several words from the 16-bit keys the score launch stored, re-read
+    # per word, and samples them from the compact sample
+    w = _small(**kw)
+    assert (w.ctx_cap + 31) // 32 > 1024
+    dc = device_case(w)
+    inp = synth.step_inputs(w, 0, dc.pre)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
+    step_on_device(dc, 0, inp, out)
+    for b in range(w.batch):
+        _check_step(w, dc, oracle_state(w, dc.pre, b), inp, out, 0, b, w.ctx)
+
+
 def test_planted_tokens_are_found():
     # sanity of the synthetic workload, not a parity bar: with a shift of 4
     # score standard deviations nearly every planted token is selected
