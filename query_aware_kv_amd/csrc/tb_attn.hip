@@ -155,18 +155,18 @@ template <typename T, int D, int GQ> constexpr bool attn_windowed_ok()
     return sizeof(T) == 2 && D == 128 && GQ >= 2;
 }
 
-template <typename T, int D, int GQ, bool BITMAP, int WIN, bool APPEND>
+template <typename T, int D, int GQ, bool BITMAP, int WIN, bool APPEND, int CH>
 __global__ __launch_bounds__(kAttnThreads)
 __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kernel(AttnArgs a)
 {
     constexpr int EPL = 16 / (int)sizeof(T); // elements per lane piece
     constexpr int LPR = D / EPL;             // lanes per row
     constexpr int RPW = 64 / LPR;            // rows per wave step
-    constexpr int NWD = kAttnChunk / 32;     // bitmap words per head
+    constexpr int NWD = CH / 32;             // bitmap words per head
     constexpr int RIF = rows_in_flight<WIN>();
     static_assert(GQ <= kAttnWaves && kAttnWaves % GQ == 0, "whole waves per query head");
     constexpr int WPH = kAttnWaves / GQ;     // waves per query head
-    constexpr int PW = kAttnChunk / WPH;     // positions of one wave's part of the chunk
+    constexpr int PW = CH / WPH;             // positions of one wave's part of the chunk
     static_assert(PW % 64 == 0, "parts of whole 64-position masks");
 
     __shared__ uint32_t bm[GQ][NWD];
@@ -175,11 +175,14 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
     __shared__ float mrg_l[GQ][WPH];
     __shared__ float mrg_acc[GQ][WPH][D];
     // the append work-group uses the merge's LDS, which it never reaches
+    // chunks of a row: at most 64 of 1024 positions (rows up to 64K), else
+    // at most kMaxCtxCap / CH
+    constexpr int NCH = (CH == kAttnChunk ? 65536 : kMaxCtxCap) / CH;
     __shared__ union {
-        CombineLds<GQ, kAttnThreads> c;
+        CombineLds<GQ, kAttnThreads, NCH> c;
         AppendLds<T, D> app;
     } shu;
-    CombineLds<GQ, kAttnThreads> &cmb = shu.c;
+    CombineLds<GQ, kAttnThreads, NCH> &cmb = shu.c;
 
     const T *__restrict__ q = (const T *)a.q;
     const T *__restrict__ kc = (const T *)a.k;
@@ -207,12 +210,12 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
         b = blockIdx.z;
         nchunk = gridDim.x;
     }
-    const int c0 = c * kAttnChunk;
+    const int c0 = c * CH;
     // The work-group's 32 bitmap words: in bitmap mode the words c,
     // c + nchunk, c + 2 nchunk, ... of the row (so every work-group takes an
     // equal share of any dense region: an always-kept window, the sink, new
     // tokens); in list mode the contiguous words of positions
-    // [c0, c0 + kAttnChunk).  A chunk-local position 32 k + j (word k, bit j)
+    // [c0, c0 + CH).  A chunk-local position 32 k + j (word k, bit j)
     // is row position 32 gword(k) + j.
     auto gword = [&](int k) { return BITMAP ? c + nchunk * k : c * NWD + k; };
     auto gpos = [&](uint32_t local) {
@@ -253,9 +256,9 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
     const int kf_raw = a.keep_from != nullptr ? a.keep_from[b] : a.cap;
     const int n = clamp_len(a.ctx_len[b], a.cap);
     // positions of the chunk are below c1 (and those of a word below n)
-    const int c1 = BITMAP ? n : min(c0 + kAttnChunk, n);
+    const int c1 = BITMAP ? n : min(c0 + CH, n);
     const bool active = BITMAP ? 32 * c < n : c0 < n;
-    const int nact = BITMAP ? min(nchunk, (n + 31) / 32) : (n + kAttnChunk - 1) / kAttnChunk;
+    const int nact = BITMAP ? min(nchunk, (n + 31) / 32) : (n + CH - 1) / CH;
 
     if (active) {
         // ---- 1. the wave's membership words ----
@@ -438,7 +441,7 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
     }
 
     // ---- 5. arrival; the last work-group of this (b, g) merges the chunks ----
-    arrive_and_combine<T, D, GQ, kAttnThreads, kMaxChunks>(
+    arrive_and_combine<T, D, GQ, kAttnThreads, NCH>(
         cmb, &a.counters[(size_t)b * a.Hkv + g], a.part_o, a.part_ml, nchunk,
         nact, head0, (T *)a.out);
 }
@@ -448,8 +451,8 @@ constexpr int kAttnWindowPairs = 2;
 
 
 
-template <typename T, int D, int GQ, bool BITMAP, bool APPEND>
-hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
+template <typename T, int D, int GQ, bool BITMAP, bool APPEND, int CH>
+hipError_t attn_launch_ch(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
     const int nchunk = attn_chunks(s.ctx_cap);
     const dim3 grid = APPEND ? dim3((nchunk + 1) * s.n_kv_heads * s.batch)
@@ -462,18 +465,26 @@ hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
     const hipError_t e = device_cus(cus);
     if (e != hipSuccess)
         return e;
-    const long wgs = (long)attn_chunks(s.ctx_cap) * s.n_kv_heads * s.batch;
+    const long wgs = (long)nchunk * s.n_kv_heads * s.batch;
     bool windowed = false;
     if constexpr (attn_windowed_ok<T, D, GQ>())
         windowed = wgs >= 2L * cus;
     if constexpr (attn_windowed_ok<T, D, GQ>())
         if (windowed)
-            hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, kAttnWindowPairs, APPEND>), grid,
+            hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, kAttnWindowPairs, APPEND, CH>), grid,
                                dim3(kAttnThreads), 0, st, a);
     if (!windowed)
-        hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, 0, APPEND>), grid, dim3(kAttnThreads),
-                           0, st, a);
+        hipLaunchKernelGGL((attn_kernel<T, D, GQ, BITMAP, 0, APPEND, CH>), grid,
+                           dim3(kAttnThreads), 0, st, a);
     return hipGetLastError();
+}
+
+template <typename T, int D, int GQ, bool BITMAP, bool APPEND>
+hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
+{
+    if (attn_chunk_len(s.ctx_cap) == 2 * kAttnChunk)
+        return attn_launch_ch<T, D, GQ, BITMAP, APPEND, 2 * kAttnChunk>(s, a, st);
+    return attn_launch_ch<T, D, GQ, BITMAP, APPEND, kAttnChunk>(s, a, st);
 }
 
 template <typename T, int D, int GQ>

@@ -169,7 +169,10 @@ struct WsLayout {
     size_t total;
 };
 
-inline int attn_chunks(int cap) { return (cap + kAttnChunk - 1) / kAttnChunk; }
+// Positions per sparse attention work-group: twice kAttnChunk past 64K
+// positions, so that the last work-group of a KV head merges fewer partials.
+inline int attn_chunk_len(int cap) { return cap > 65536 ? 2 * kAttnChunk : kAttnChunk; }
+inline int attn_chunks(int cap) { return (cap + attn_chunk_len(cap) - 1) / attn_chunk_len(cap); }
 inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 
 inline int dense_chunks(int cap) { return (cap + kDenseChunk - 1) / kDenseChunk; }

@@ -299,18 +299,21 @@ def test_ragged_batch_fused(kw):
     dict(batch=40, n_q_heads=16, n_kv_heads=2, n_imp_heads=4, n_sink=4, n_local=64),
     # 2 query heads per KV head, one importance head each
     dict(batch=20, n_q_heads=8, n_kv_heads=4, n_imp_heads=8),
-], ids=["group8", "group2"])
+    # past 64K positions a work-group takes 2048 of them
+    dict(ctx0=70000, budget=2000, batch=16, n_q_heads=8, n_kv_heads=2, n_imp_heads=8),
+], ids=["group8", "group2", "long_chunks"])
 def test_windowed_attention_walk(kw):
     # a grid of at least two work-groups per compute unit: the bitmap
     # attention walks its rows in barrier-separated windows; ragged lengths
     # leave some chunks with no positions and others ending mid-word
-    w = _small(ctx0=7000, budget=300, **kw)
-    wgs = -(-w.ctx_cap // 1024) * w.n_kv_heads * w.batch
+    w = _small(**{"ctx0": 7000, "budget": 300, **kw})
+    chunk = 2048 if w.ctx_cap > 65536 else 1024
+    wgs = -(-w.ctx_cap // chunk) * w.n_kv_heads * w.batch
     assert wgs >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
     dc = device_case(w)
     inp = synth.step_inputs(w, 0, dc.pre)
     lens = [w.ctx_cap] * w.batch
-    lens[:4] = [1, 33, 1025, 5000]
+    lens[:4] = [1, 33, chunk + 1, w.ctx_cap - 2000]
     ctx = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dc.K.dtype, device="cuda")
     args = tbl.step_args(dc.shape, dc.params, q=inp.q.cuda(), q_imp=inp.q_imp.cuda(),
