@@ -578,6 +578,10 @@ def main() -> int:
                          "batch-4 16K interval, 128K)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for HBM counter scaling)")
+    ap.add_argument("--workload", choices=[TINY_F32.name, BATCHED_8K.name, INTERVAL_16K.name,
+                                           LONG_128K.name],
+                    help="time only this workload's leg and print its JSON object (for "
+                         "per-workload kernel traces)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
@@ -587,9 +591,20 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
 
+    torch.cuda.set_device(0)
+    if a.workload:
+        wl = BY_NAME[a.workload]
+        leg = {BATCHED_8K.name: lambda: layers_leg(wl, max(3, a.steps // 20)),
+               INTERVAL_16K.name: lambda: interval_leg(wl)}.get(wl.name,
+                                                              lambda: single_step_leg(wl, a.steps))
+        res = leg()
+        if not a.no_cpu_baseline:
+            res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+        print(json.dumps(res), flush=True)
+        return 0
+
     w = replace(LLAMA_32K, n_sink=a.n_sink, n_local=a.n_local)
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     log(f"bench: generating {w.name}")
     pre = synth.prefill(w)
     inp = synth.step_inputs(w, 0, pre)
