@@ -331,6 +331,42 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
 int tb_decode_step_noalloc(const tb_shape *shape, const tb_select_params *params,
                            const tb_step_args *args, void *stream);
 
+/*
+ * Debug mode (TB_CHECK).  Off by default; the environment variable TB_CHECK
+ * set to anything but "" or "0" turns it on when the library is first used,
+ * and tb_set_check() overrides that.  While it is on, every call enqueues
+ * small check kernels on its stream before its own kernels; each failed
+ * check ORs its bit into a word kept on the device (one per GPU).  The hot
+ * path itself never faults on the conditions checked here -- it clamps
+ * context lengths, list counts and list entries, and produces garbage from
+ * non-finite inputs -- so the bits say why a result may be wrong.
+ *   TB_CHECK_NONFINITE_INPUT  a NaN or infinity in q, q_imp, k_new, v_new,
+ *                             w (tb_predict_queries: h, w1, w2)
+ *   TB_CHECK_NONFINITE_CACHE  ... in the rows [0, ctx_len) of the K, V or
+ *                             projected-key cache that the call reads (in
+ *                             tb_decode_step the rows before the appended
+ *                             ones; in tb_project_keys the whole key cache)
+ *   TB_CHECK_CTX_RANGE        ctx_len[b] outside [0, ctx_cap]
+ *   TB_CHECK_KEEP_RANGE       keep_from[b] outside [0, ctx_cap] (attention)
+ *   TB_CHECK_SEL_RANGE        a list count outside [0, sel_stride], or a list
+ *                             entry outside [0, ctx_cap) or not ascending
+ *                             (tb_sparse_attn with lists)
+ *   TB_CHECK_NONFINITE_SCORES a NaN or infinity among the scores of
+ *                             [0, ctx_len) (tb_select)
+ * tb_check_flags waits for the device (hipDeviceSynchronize), stores the
+ * current device's word in *flags and, if clear is non-zero, resets it to
+ * 0.  Returns TB_OK, TB_EINVAL (flags NULL) or TB_EHIP.
+ */
+#define TB_CHECK_NONFINITE_INPUT 1u
+#define TB_CHECK_NONFINITE_CACHE 2u
+#define TB_CHECK_CTX_RANGE 4u
+#define TB_CHECK_KEEP_RANGE 8u
+#define TB_CHECK_SEL_RANGE 16u
+#define TB_CHECK_NONFINITE_SCORES 32u
+void tb_set_check(int on);
+int tb_check_enabled(void);
+int tb_check_flags(uint32_t *flags, int clear);
+
 #ifdef __cplusplus
 }
 #endif

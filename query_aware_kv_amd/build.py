@@ -17,7 +17,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtokenbutler.so")
 
 SOURCES = ["tb_api.hip", "tb_project.hip", "tb_score.hip", "tb_select.hip", "tb_attn.hip",
-           "tb_dense.hip", "tb_mlp.hip"]
+           "tb_dense.hip", "tb_mlp.hip", "tb_check.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -62,6 +62,34 @@ int32_t sel_capacity(const tb_shape &s, const tb_select_params &p)
 
 int hip_rc(hipError_t e) { return e == hipSuccess ? TB_OK : TB_EHIP; }
 
+// Debug mode: the checks of a fused step's inputs (the caches' rows before
+// the appended ones, and keep_from only where it is read: on reuse steps).
+int check_step_inputs(const tb_shape &s, const tb_step_args &a, hipStream_t st)
+{
+    const int dt = s.dtype;
+    const size_t kv_new = (size_t)s.batch * s.n_kv_heads * a.n_new * s.head_dim;
+    const hipError_t es[] = {
+        check_dense(a.q, (size_t)s.batch * s.n_q_heads * s.head_dim, dt, TB_CHECK_NONFINITE_INPUT, st),
+        a.refresh ? check_dense(a.q_imp, (size_t)s.batch * s.n_imp_heads * s.d_imp, dt,
+                                TB_CHECK_NONFINITE_INPUT, st)
+                  : hipSuccess,
+        check_dense(a.k_new, kv_new, dt, TB_CHECK_NONFINITE_INPUT, st),
+        check_dense(a.v_new, kv_new, dt, TB_CHECK_NONFINITE_INPUT, st),
+        check_dense(a.w, (size_t)s.head_dim * s.d_imp, dt, TB_CHECK_NONFINITE_INPUT, st),
+        check_cache(a.k_cache, a.ctx_len, a.n_new, s.batch, s.n_kv_heads, s.ctx_cap, s.head_dim,
+                    dt, TB_CHECK_NONFINITE_CACHE, st),
+        check_cache(a.v_cache, a.ctx_len, a.n_new, s.batch, s.n_kv_heads, s.ctx_cap, s.head_dim,
+                    dt, TB_CHECK_NONFINITE_CACHE, st),
+        check_cache(a.kp_cache, a.ctx_len, a.n_new, s.batch, s.n_kv_heads, s.ctx_cap, s.d_imp, dt,
+                    TB_CHECK_NONFINITE_CACHE, st),
+        check_indices(a.ctx_len, a.refresh ? nullptr : a.keep_from, s.batch, s.n_imp_heads,
+                      s.ctx_cap, nullptr, 0, nullptr, st)};
+    for (hipError_t e : es)
+        if (e != hipSuccess)
+            return TB_EHIP;
+    return TB_OK;
+}
+
 struct Ws {
     float *scores;
     float *part_o;
@@ -286,6 +314,14 @@ int tb_project_keys(const tb_shape *shape, const void *k_cache, const void *w,
         return TB_OK;
     if ((long long)shape->batch * shape->n_kv_heads * n_tokens > 0x7fffffffLL)
         return TB_EINVAL;
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        TB_TRY(hip_rc(check_dense(w, (size_t)shape->head_dim * shape->d_imp, shape->dtype,
+                                  TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_cache(k_cache, nullptr, 0, shape->batch, shape->n_kv_heads,
+                                  shape->ctx_cap, shape->head_dim, shape->dtype,
+                                  TB_CHECK_NONFINITE_CACHE, st)));
+    }
     return hip_rc(launch_project(*shape, k_cache, w, pos0, n_tokens, kp_cache,
                                  (hipStream_t)stream));
 }
@@ -300,6 +336,16 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        TB_TRY(hip_rc(check_dense(q_imp, (size_t)shape->batch * shape->n_imp_heads * shape->d_imp,
+                                  shape->dtype, TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_cache(kp_cache, ctx_len, 0, shape->batch, shape->n_kv_heads,
+                                  shape->ctx_cap, shape->d_imp, shape->dtype,
+                                  TB_CHECK_NONFINITE_CACHE, st)));
+        TB_TRY(hip_rc(check_indices(ctx_len, nullptr, shape->batch, shape->n_imp_heads,
+                                    shape->ctx_cap, nullptr, 0, nullptr, st)));
+    }
     return hip_rc(launch_score(*shape, q_imp, const_cast<void *>(kp_cache), ctx_len, scores, 0,
                                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                                (hipStream_t)stream));
@@ -318,6 +364,13 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        TB_TRY(hip_rc(check_cache(scores, ctx_len, 0, shape->batch, shape->n_imp_heads,
+                                  shape->ctx_cap, 1, TB_F32, TB_CHECK_NONFINITE_SCORES, st)));
+        TB_TRY(hip_rc(check_indices(ctx_len, nullptr, shape->batch, shape->n_imp_heads,
+                                    shape->ctx_cap, nullptr, 0, nullptr, st)));
+    }
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
                                 sel_capacity(*shape, *params), sel_count, topb_idx, sel_bits,
                                 nullptr, 0, nullptr, nullptr, (hipStream_t)stream));
@@ -341,6 +394,19 @@ int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        const tb_shape &s = *shape;
+        TB_TRY(hip_rc(check_dense(q, (size_t)s.batch * s.n_q_heads * s.head_dim, s.dtype,
+                                  TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_cache(k_cache, ctx_len, 0, s.batch, s.n_kv_heads, s.ctx_cap,
+                                  s.head_dim, s.dtype, TB_CHECK_NONFINITE_CACHE, st)));
+        TB_TRY(hip_rc(check_cache(v_cache, ctx_len, 0, s.batch, s.n_kv_heads, s.ctx_cap,
+                                  s.head_dim, s.dtype, TB_CHECK_NONFINITE_CACHE, st)));
+        TB_TRY(hip_rc(check_indices(ctx_len, keep_from, s.batch, s.n_imp_heads, s.ctx_cap,
+                                    sel_bits == nullptr ? sel_idx : nullptr, sel_stride,
+                                    sel_count, st)));
+    }
     Ws W = carve(ws, L);
     return hip_rc(launch_attn(*shape, q, k_cache, v_cache, sel_idx, sel_stride, sel_count,
                               sel_bits, keep_from, ctx_len, softmax_scale, out, W.part_o,
@@ -361,6 +427,18 @@ int tb_dense_attn(const tb_shape *shape, const void *q, const void *k_cache, con
         return TB_EINVAL;
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        const tb_shape &s = *shape;
+        TB_TRY(hip_rc(check_dense(q, (size_t)s.batch * s.n_q_heads * s.head_dim, s.dtype,
+                                  TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_cache(k_cache, ctx_len, 0, s.batch, s.n_kv_heads, s.ctx_cap,
+                                  s.head_dim, s.dtype, TB_CHECK_NONFINITE_CACHE, st)));
+        TB_TRY(hip_rc(check_cache(v_cache, ctx_len, 0, s.batch, s.n_kv_heads, s.ctx_cap,
+                                  s.head_dim, s.dtype, TB_CHECK_NONFINITE_CACHE, st)));
+        TB_TRY(hip_rc(check_indices(ctx_len, nullptr, s.batch, s.n_imp_heads, s.ctx_cap, nullptr,
+                                    0, nullptr, st)));
+    }
     Ws W = carve(ws, L);
     return hip_rc(launch_dense(*shape, q, k_cache, v_cache, ctx_len, softmax_scale, out, W.part_o,
                                W.part_ml, W.counters, (hipStream_t)stream));
@@ -385,6 +463,16 @@ int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1,
         return TB_EINVAL;
     if (ws_bytes < mlp_layout(*shape).total)
         return TB_EWORKSPACE;
+    if (check_enabled()) {
+        const hipStream_t st = (hipStream_t)stream;
+        const tb_mlp_shape &s = *shape;
+        const size_t N = (size_t)s.n_slots * s.n_imp_heads * s.d_imp;
+        TB_TRY(hip_rc(check_dense(h, (size_t)s.tokens * s.hidden, s.dtype,
+                                  TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_dense(w1, (size_t)s.inner * s.hidden, s.dtype,
+                                  TB_CHECK_NONFINITE_INPUT, st)));
+        TB_TRY(hip_rc(check_dense(w2, N * s.inner, s.dtype, TB_CHECK_NONFINITE_INPUT, st)));
+    }
     return hip_rc(launch_mlp(*shape, h, w1, w2, q_imp, ws, (hipStream_t)stream));
 }
 
@@ -394,6 +482,8 @@ int tb_decode_step(const tb_shape *shape, const tb_select_params *params,
     TB_TRY(check_step(shape, params, a));
     WsLayout L;
     TB_TRY(check_ws(*shape, ws, ws_bytes, &L));
+    if (check_enabled())
+        TB_TRY(check_step_inputs(*shape, *a, (hipStream_t)stream));
     return decode_step_run(*shape, *params, *a, ws, L, (hipStream_t)stream);
 }
 
@@ -411,7 +501,20 @@ int tb_decode_step_noalloc(const tb_shape *shape, const tb_select_params *params
     // words that must start at zero are cleared by a kernel (not a memset
     // node, so that the call can be captured in a graph)
     TB_TRY(hip_rc(launch_zero_words((uint32_t *)((char *)ws + L.zeroed), L.zeroed_words, st)));
+    if (check_enabled())
+        TB_TRY(check_step_inputs(*shape, *a, st));
     return decode_step_run(*shape, *params, *a, ws, L, st);
+}
+
+void tb_set_check(int on) { set_check(on != 0); }
+
+int tb_check_enabled(void) { return check_enabled() ? 1 : 0; }
+
+int tb_check_flags(uint32_t *flags, int clear)
+{
+    if (flags == nullptr)
+        return TB_EINVAL;
+    return hip_rc(read_check_flags(flags, clear != 0));
 }
 
 } // extern "C"

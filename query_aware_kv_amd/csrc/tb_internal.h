@@ -226,6 +226,21 @@ inline WsLayout ws_layout(const tb_shape &s)
 // Compute units of the current device, queried once per device.
 hipError_t device_cus(int &cus);
 
+// Debug mode (TB_CHECK): check kernels that OR TB_CHECK_* bits into the
+// device's check word; the caller enqueues them only when check_enabled().
+bool check_enabled();
+void set_check(bool on);
+// every element of a dense array of n elements (dtype TB_F32 / TB_BF16)
+hipError_t check_dense(const void *p, size_t n, int dtype, uint32_t bit, hipStream_t st);
+// rows [0, len[b] - minus) of a cache [b][heads][cap][row] (len NULL: all)
+hipError_t check_cache(const void *c, const int32_t *len, int minus, int batch, int heads,
+                       int cap, int row, int dtype, uint32_t bit, hipStream_t st);
+// ctx_len / keep_from ranges, and with sel_idx the lists' counts and entries
+hipError_t check_indices(const int32_t *ctx_len, const int32_t *keep_from, int batch, int Himp,
+                         int cap, const int32_t *sel_idx, int stride, const int32_t *sel_count,
+                         hipStream_t st);
+hipError_t read_check_flags(uint32_t *out, bool clear);
+
 // Each returns hipSuccess or the launch error.  Shapes are already validated.
 hipError_t launch_project(const tb_shape &s, const void *k_cache, const void *w,
                           const int32_t *pos0, int n_tokens, void *kp_cache, hipStream_t st);

@@ -91,6 +91,11 @@ def lib() -> ctypes.CDLL:
         L.tb_mlp_workspace_bytes.restype = ctypes.c_size_t
         L.tb_predict_queries.argtypes = [P(MlpShape), _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                          _vp]
+        L.tb_set_check.argtypes = [ctypes.c_int]
+        L.tb_set_check.restype = None
+        L.tb_check_enabled.restype = ctypes.c_int
+        L.tb_check_flags.argtypes = [P(ctypes.c_uint32), ctypes.c_int]
+        L.tb_check_flags.restype = ctypes.c_int
         for fn in ("tb_project_keys", "tb_score", "tb_select", "tb_sparse_attn",
                    "tb_dense_attn", "tb_decode_step", "tb_decode_step_noalloc",
                    "tb_predict_queries"):
@@ -357,3 +362,28 @@ def decode_step_noalloc(shape, params, args: StepArgs, stream=None):
     """tb_decode_step on the library's fixed device scratch (no workspace)."""
     _check("tb_decode_step_noalloc", lib().tb_decode_step_noalloc(
         ctypes.byref(shape), ctypes.byref(params), ctypes.byref(args), _stream(stream)))
+
+
+# debug mode (TB_CHECK): bits of the device's check word
+CHECK_NONFINITE_INPUT = 1
+CHECK_NONFINITE_CACHE = 2
+CHECK_CTX_RANGE = 4
+CHECK_KEEP_RANGE = 8
+CHECK_SEL_RANGE = 16
+CHECK_NONFINITE_SCORES = 32
+
+
+def set_check(on: bool) -> None:
+    """Turn the debug-mode input checks on or off (overrides TB_CHECK)."""
+    lib().tb_set_check(int(bool(on)))
+
+
+def check_enabled() -> bool:
+    return bool(lib().tb_check_enabled())
+
+
+def check_flags(clear: bool = True) -> int:
+    """Wait for the device and return its check word (cleared if asked)."""
+    v = ctypes.c_uint32(0)
+    _check("tb_check_flags", lib().tb_check_flags(ctypes.byref(v), int(bool(clear))))
+    return int(v.value)

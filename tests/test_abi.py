@@ -226,3 +226,25 @@ def test_noalloc_step_rejects_a_shape_beyond_its_scratch_on_the_host():
     bad = _shape(head_dim=96)
     assert tbl.lib().tb_decode_step_noalloc(ctypes.byref(bad), ctypes.byref(params),
                                             ctypes.byref(args), None) == tbl.TB_EUNSUPPORTED
+
+
+def test_check_mode_switch_and_flag_argument():
+    # the switch is host state; a NULL destination is rejected before any HIP call
+    was = tbl.check_enabled()
+    try:
+        tbl.set_check(True)
+        assert tbl.check_enabled()
+        tbl.set_check(False)
+        assert not tbl.check_enabled()
+    finally:
+        tbl.set_check(was)
+    assert tbl.lib().tb_check_flags(None, 0) == tbl.TB_EINVAL
+
+
+@pytest.mark.parametrize("value,on", [("1", True), ("yes", True), ("0", False), ("", False)])
+def test_check_mode_from_the_environment(value, on):
+    code = ("from query_aware_kv_amd import tokenbutler as t; "
+            "print(int(t.check_enabled()))")
+    env = dict(os.environ, TB_CHECK=value)
+    out = subprocess.check_output(["python3", "-c", code], cwd=ROOT, env=env).decode().strip()
+    assert out == str(int(on))
