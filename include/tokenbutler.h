@@ -255,9 +255,12 @@ size_t tb_mlp_workspace_bytes(const tb_mlp_shape *shape);
  * layer's weight), q_imp [G][M][Himp][d]: slot g is the q_imp argument of
  * tb_score / tb_decode_step for its consumer layer (batch = M).  No biases.
  * Products are accumulated in fp32 on the matrix cores; round() is to the
- * dtype, nearest even.  h, w1, w2 16-byte aligned; the workspace (at least
- * tb_mlp_workspace_bytes(), 256-byte aligned, no initial contents needed)
- * holds the hidden layer.
+ * dtype, nearest even.  h, w1, w2 16-byte aligned.  The workspace (at least
+ * tb_mlp_workspace_bytes(), 256-byte aligned) holds the hidden layer and,
+ * for layers with few output columns, partial sums over parts of k and
+ * their arrival counters: it must be zero-filled before its first use, and
+ * every completed call leaves the counters zero again.  Calls sharing a
+ * workspace must not overlap.
  * Errors: TB_EINVAL, TB_EUNSUPPORTED, TB_EWORKSPACE, TB_EHIP.
  */
 int tb_predict_queries(const tb_mlp_shape *shape, const void *h, const void *w1, const void *w2,

@@ -9,27 +9,6 @@ namespace tb {
 
 constexpr int kMaxChunks = kMaxCtxCap / kAttnChunk;
 
-// Chunk partials cross work-groups (and XCDs, whose L2 caches are not
-// coherent with each other).  They are written and read with agent-scope
-// atomic accesses, which go through to the device coherence point, so no
-// full L2 write-back fence is needed to publish them.
-// Two 64-bit accesses per four floats: every agent-scope access is its own
-// memory transaction, so wider ones matter.
-__device__ __forceinline__ float4 load4_agent(const float *p)
-{
-    const double x = __hip_atomic_load(reinterpret_cast<const double *>(p), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    const double y = __hip_atomic_load(reinterpret_cast<const double *>(p) + 1,
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float2 lo = __builtin_bit_cast(float2, x), hi = __builtin_bit_cast(float2, y);
-    return make_float4(lo.x, lo.y, hi.x, hi.y);
-}
-__device__ __forceinline__ void store2_agent(float *p, float x, float y)
-{
-    __hip_atomic_store(reinterpret_cast<double *>(p), __builtin_bit_cast(double, make_float2(x, y)),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Sum of x over aligned groups of N lanes (N in {1, 2, 4, 8, 16, 32}); every
 // lane of the group receives the sum.  Within a 16-lane DPP row the partners
 // come from quad permutations and the half/full row mirrors.

@@ -86,6 +86,27 @@ __device__ __forceinline__ void lds_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Partial results that cross work-groups (and XCDs, whose L2 caches are
+// not coherent with each other): attention chunk partials, split-k MLP tiles.  They are written and read with agent-scope
+// atomic accesses, which go through to the device coherence point, so no
+// full L2 write-back fence is needed to publish them.
+// Two 64-bit accesses per four floats: every agent-scope access is its own
+// memory transaction, so wider ones matter.
+__device__ __forceinline__ float4 load4_agent(const float *p)
+{
+    const double x = __hip_atomic_load(reinterpret_cast<const double *>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    const double y = __hip_atomic_load(reinterpret_cast<const double *>(p) + 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float2 lo = __builtin_bit_cast(float2, x), hi = __builtin_bit_cast(float2, y);
+    return make_float4(lo.x, lo.y, hi.x, hi.y);
+}
+__device__ __forceinline__ void store2_agent(float *p, float x, float y)
+{
+    __hip_atomic_store(reinterpret_cast<double *>(p), __builtin_bit_cast(double, make_float2(x, y)),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // The same for the lanes of one wave: the wave's LDS operations have
 // completed, so other lanes of the wave read what it wrote.
 __device__ __forceinline__ void wave_lds_sync()
@@ -287,8 +308,18 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
 constexpr int kMlpKGrain = 256; // K of both layers is a multiple of this
 struct MlpLayout {
     size_t hidden; // [M][F] hidden layer in the dtype
+    size_t part;   // k-split partial tiles fp32 [tiles][splits][M/16][64][4]
+    size_t counters; // k-split arrival counters u32 [tiles] (kept zero)
     size_t total;
 };
+// k-splits of an MLP layer with N outputs and K inputs: layers with fewer
+// than 128 column tiles of 16 are split four ways over K (when K is a whole
+// number of 256-value chunks per split), so that the launch spreads over
+// the chip.
+inline int mlp_splits(int N, int K)
+{
+    return N / 16 < 128 && K % (4 * 256) == 0 ? 4 : 1;
+}
 MlpLayout mlp_layout(const tb_mlp_shape &s);
 hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, const void *w2,
                       void *q_imp, void *ws, hipStream_t st);

@@ -46,6 +46,9 @@ struct LayerArgs {
     int M, K, N;
     int slot;           // columns per slot of a slot-major output (0: row-major)
     int act;            // TB_ACT_RELU / TB_ACT_SILU, or -1 for none
+    int splits;         // work-groups per column tile, each K / splits of the sum
+    f32x4 *part;        // their partial tiles (splits > 1)
+    uint32_t *counters; // one arrival counter per column tile, kept zero
 };
 
 __device__ __forceinline__ float activate(float x, int act)
@@ -80,7 +83,9 @@ __global__ __launch_bounds__(64 * kMlpMaxWaves) void mlp_layer_kernel(LayerArgs 
     extern __shared__ f32x4 tiles[];         // [waves][MT][64]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nwaves = (int)blockDim.x / 64;
-    const int n0 = blockIdx.x * kMlpCols;
+    const int tile = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+    const int n0 = tile * kMlpCols;
+    const int kbeg = split * (a.K / a.splits), kend = kbeg + a.K / a.splits;
     const int r = lane & 15, q4 = lane >> 4;
 
     const T *wrow = (const T *)a.w + (size_t)(n0 + r) * a.K + EPL * q4;
@@ -96,8 +101,9 @@ __global__ __launch_bounds__(64 * kMlpMaxWaves) void mlp_layer_kernel(LayerArgs 
     for (int t = 0; t < MT; ++t)
         acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // this wave's slice: 256-value chunks wave, wave + nwaves, ...
-    for (int k0 = wave * kMlpKGrain; k0 < a.K; k0 += nwaves * kMlpKGrain) {
+    // this wave's slice of the work-group's k range: 256-value chunks wave,
+    // wave + nwaves, ...
+    for (int k0 = kbeg + wave * kMlpKGrain; k0 < kend; k0 += nwaves * kMlpKGrain) {
         for (int k = k0; k < k0 + kMlpKGrain; k += CHUNK) {
             uint4 bp[UNR], ap[MT][UNR];
 #pragma unroll
@@ -140,18 +146,60 @@ __global__ __launch_bounds__(64 * kMlpMaxWaves) void mlp_layer_kernel(LayerArgs 
     if (wave != 0)
         return;
     const int n = n0 + r;
+    f32x4 sum[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-        f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < nwaves; ++w)
-            sum += tiles[(w * MT + t) * 64 + lane];
+            sum[t] += tiles[(w * MT + t) * 64 + lane];
+    }
+    if (a.splits > 1) {
+        // Split over k: the work-group publishes its partial tiles with
+        // device-coherent stores and, once they are complete, counts its
+        // arrival; the last of the tile's work-groups adds the partials in
+        // split order (the sum does not depend on arrival order) and
+        // finishes the tile.  Same ordering argument as the attention's
+        // cross-chunk merge; the last arriver resets the counter.
+        f32x4 *mine = a.part + ((size_t)(tile * a.splits + split) * MT) * 64;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2)
+                store2_agent(reinterpret_cast<float *>(&mine[t * 64 + lane]) + i, sum[t][i],
+                             sum[t][i + 1]);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        uint32_t old = 0u;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&a.counters[tile], 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old != (uint32_t)(a.splits - 1))
+            return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0)
+            __hip_atomic_store(&a.counters[tile], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const f32x4 *parts = a.part + ((size_t)tile * a.splits * MT) * 64;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            f32x4 acc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int sp = 0; sp < a.splits; ++sp) {
+                const float4 v = load4_agent(
+                    reinterpret_cast<const float *>(&parts[(sp * MT + t) * 64 + lane]));
+                acc4 += f32x4{v.x, v.y, v.z, v.w};
+            }
+            sum[t] = acc4;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 16 * t + 4 * q4 + i;
             if (m < a.M)
-                store_out<T>(a, m, n, sum[i]);
+                store_out<T>(a, m, n, sum[t][i]);
         }
-    }
 }
 
 // One token: wave v of the work-group owns weight rows R * (4 * blockIdx.x
@@ -236,9 +284,9 @@ hipError_t layer_t(const LayerArgs &a, hipStream_t st)
     const hipError_t g = gemv_t<T>(a, st);
     if (g != hipErrorNotSupported)
         return g;
-    const int chunks = a.K / kMlpKGrain;
+    const int chunks = a.K / kMlpKGrain / a.splits;
     const int waves = chunks < kMlpMaxWaves ? chunks : kMlpMaxWaves;
-    const dim3 grid(a.N / kMlpCols);
+    const dim3 grid(a.N / kMlpCols * a.splits);
     const int mt = (a.M + 15) / 16;
     const size_t lds = (size_t)waves * mt * 64 * sizeof(f32x4);
     switch (mt) {
@@ -262,8 +310,26 @@ MlpLayout mlp_layout(const tb_mlp_shape &s)
 {
     MlpLayout L;
     const size_t elt = s.dtype == TB_BF16 ? 2 : 4;
+    const int N = s.n_slots * s.n_imp_heads * s.d_imp;
+    const int mt = (s.tokens + 15) / 16;
+    // partial tiles and counters for whichever layer is split the most
+    size_t part = 0, tiles = 0;
+    const int dims[2][2] = {{s.inner, s.hidden}, {N, s.inner}};
+    for (const auto &nk : dims) {
+        const int sp = mlp_splits(nk[0], nk[1]);
+        const size_t t = (size_t)(nk[0] / 16);
+        if (sp > 1) {
+            part = part > t * sp ? part : t * sp;
+            tiles = tiles > t ? tiles : t;
+        }
+    }
     L.hidden = 0;
-    L.total = align_up((size_t)s.tokens * s.inner * elt);
+    size_t off = align_up((size_t)s.tokens * s.inner * elt);
+    L.part = off;
+    off += align_up(part * mt * 64 * sizeof(f32x4));
+    L.counters = off;
+    off += align_up(tiles * sizeof(uint32_t));
+    L.total = off;
     return L;
 }
 
@@ -282,6 +348,9 @@ hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, cons
     a.N = s.inner;
     a.slot = 0;
     a.act = s.act;
+    a.part = (f32x4 *)(base + L.part);
+    a.counters = (uint32_t *)(base + L.counters);
+    a.splits = s.tokens > 1 ? mlp_splits(a.N, a.K) : 1;
     hipError_t e = layer(s, a, st);
     if (e != hipSuccess)
         return e;
@@ -292,6 +361,7 @@ hipError_t launch_mlp(const tb_mlp_shape &s, const void *h, const void *w1, cons
     a.N = N;
     a.slot = s.n_imp_heads * s.d_imp;
     a.act = -1;
+    a.splits = s.tokens > 1 ? mlp_splits(a.N, a.K) : 1;
     return layer(s, a, st);
 }
 

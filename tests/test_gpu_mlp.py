@@ -95,3 +95,22 @@ def test_mlp_slot_feeds_score():
     ref = orc.mlp(f64(inp.h), f64(inp.w1), f64(inp.w2), G, Himp, d, orc.ACT_RELU, orc.F32)
     np.testing.assert_allclose(f64(q), ref, rtol=0, atol=1e-5)
     assert q[1].is_contiguous() and tuple(q[1].shape) == (M, Himp, d)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("E,F", [(1024, 512), (512, 2048)], ids=["split_layer1", "split_layer2"])
+@pytest.mark.parametrize("M", [3, 17, 64])
+def test_mlp_split_over_k(dtype, E, F, M):
+    # layers with few output columns split k over four work-groups whose
+    # partial tiles the last one adds in split order: within the bound, the
+    # same bits on every call, and the arrival counters left at zero (the
+    # reused workspace gives the same result twice more)
+    G, Himp, d = 2, 4, 16
+    inp, q, ws = _run(M, E, F, G, Himp, d, dtype, tbl.TB_ACT_SILU)
+    _check(inp, q, G, Himp, d, dtype, tbl.TB_ACT_SILU)
+    shape = tbl.make_mlp_shape(M, E, F, G, Himp, d, dtype, tbl.TB_ACT_SILU)
+    for _ in range(2):
+        q2 = torch.empty_like(q)
+        tbl.predict_queries(shape, inp.h.cuda(), inp.w1.cuda(), inp.w2.cuda(), q2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(q, q2)
