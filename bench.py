@@ -805,7 +805,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "attn_kernel (tb_sparse_attn)",
                      "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": attn_gbs / PEAK_HBM_GBS, "traffic": measured_traffic(),
-                     "algorithmic_bytes": gather_bytes, "us_per_launch": ms_attn * 1e3},
+                     "algorithmic_bytes": gather_bytes, "us_per_launch": ms_attn * 1e3,
+                     "step": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
+                              "frac": step_gbs / PEAK_HBM_GBS}},
         "step_hbm": {"algorithmic_bytes": step_bytes, "achieved": step_gbs,
                      "frac": step_gbs / PEAK_HBM_GBS, "unique_rows": uniq,
                      "logical_rows": logical},
