@@ -532,10 +532,14 @@ def test_select_single_and_empty_contexts():
     _select_case(rows, [0, 1], 3, 1)
 
 
-def test_tie_heavy_scores_through_score_kernel():
+@pytest.mark.parametrize("kw", [dict(dtype="f32", head_dim=64, d_imp=16),
+                                dict(dtype="bf16", head_dim=128, d_imp=32, ctx0=5000, budget=400)],
+                         ids=["f32_radix", "bf16_sampled"])
+def test_tie_heavy_scores_through_score_kernel(kw):
     # integer-valued projected keys and importance queries: many exact score
-    # ties, decided by position on both sides
-    w = _small(dtype="f32", head_dim=64, d_imp=16, budget=40, radius=1, plant_per_head=0)
+    # ties, decided by position on both sides (rows under 64 words take the
+    # radix passes directly; longer ones first try the sample bracket)
+    w = _small(**{"budget": 40, "radius": 1, "plant_per_head": 0, **kw})
     pre = synth.prefill(w)
     rng = np.random.default_rng(9)
     K = np.zeros((w.batch, w.n_kv_heads, w.ctx_cap, w.head_dim), dtype=np.float32)
@@ -543,11 +547,13 @@ def test_tie_heavy_scores_through_score_kernel():
     Wm = np.zeros((w.head_dim, w.d_imp), dtype=np.float32)
     Wm[np.arange(w.d_imp), np.arange(w.d_imp)] = 1.0
     qi = rng.integers(-1, 2, size=(w.batch, w.n_imp_heads, w.d_imp)).astype(np.float32)
-    pre = replace(pre, K=torch.from_numpy(K), W=torch.from_numpy(Wm), q_imp0=torch.from_numpy(qi),
-                  k_next=torch.from_numpy(K[:, :, w.ctx0:w.ctx0 + 1].copy()))
+    dt = synth.torch_dtype(w)
+    pre = replace(pre, K=torch.from_numpy(K).to(dt), W=torch.from_numpy(Wm).to(dt),
+                  q_imp0=torch.from_numpy(qi).to(dt),
+                  k_next=torch.from_numpy(K[:, :, w.ctx0:w.ctx0 + 1].copy()).to(dt))
     dc = device_case(w, pre=pre)
     inp = synth.step_inputs(w, 0, pre)
-    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=dt, device="cuda")
     step_on_device(dc, 0, inp, out)
     for b in range(w.batch):
         st = oracle_state(w, pre, b)
