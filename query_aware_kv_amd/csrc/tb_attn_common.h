@@ -149,7 +149,13 @@ __device__ __forceinline__ void arrive_and_combine(CombineLds<GQ, THREADS, NCH> 
         S.f[hl][cc] = v.x;
         S.l[hl][cc] = v.y;
     }
-    const float *po = part_o + (head0 + chl) * nchunk * D + d4 * 4;
+    // this thread's column of the group's partials, [GQ][nchunk][D] floats
+    const __amdgpu_buffer_rsrc_t po =
+        coherent_rsrc(part_o + head0 * nchunk * D, (uint32_t)(GQ * nchunk * D * sizeof(float)));
+    const uint32_t col0 = (uint32_t)((chl * nchunk * D + d4 * 4) * sizeof(float));
+    auto part_at = [&](int cc) {
+        return load4_coherent(po, col0 + (uint32_t)((cc < nact ? cc : 0) * D * sizeof(float)));
+    };
     float4 s4 = make_float4(0.f, 0.f, 0.f, 0.f);
     // chunk weights need the maxima; the first batch of partial sums is
     // loaded meanwhile
@@ -158,7 +164,7 @@ __device__ __forceinline__ void arrive_and_combine(CombineLds<GQ, THREADS, NCH> 
 #pragma unroll
     for (int r = 0; r < BATCH; ++r) {
         const int cc = part + r * NPART;
-        v0[r] = load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
+        v0[r] = part_at(cc);
     }
     // the (max, sum) pairs are in LDS; the partial sums stay in flight
     lds_barrier();
@@ -184,7 +190,7 @@ __device__ __forceinline__ void arrive_and_combine(CombineLds<GQ, THREADS, NCH> 
 #pragma unroll
         for (int r = 0; r < BATCH; ++r) {
             const int cc = c0b + r * NPART;
-            v[r] = c0b == part ? v0[r] : load4_agent(po + (size_t)(cc < nact ? cc : 0) * D);
+            v[r] = c0b == part ? v0[r] : part_at(cc);
         }
 #pragma unroll
         for (int r = 0; r < BATCH; ++r) {

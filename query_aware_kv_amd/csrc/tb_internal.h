@@ -107,6 +107,24 @@ __device__ __forceinline__ void store2_agent(float *p, float x, float y)
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Bulk reads of such partials: 16-byte buffer loads carrying the same
+// cache-policy bit (sc1) that an agent-scope atomic load is given, so they
+// too are served from the device coherence point, at a quarter of the
+// instructions of 32-bit atomics (a 64 KB read by one work-group: 0.9 us
+// against 1.2 us with coalesced 64-bit atomic loads).  The resource covers
+// [base, base + bytes); a load past it reads zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base, uint32_t bytes)
+{
+    // stride 0, so the record count is in bytes; 32-bit data format
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ float4 load4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    constexpr int kSc1 = 16; // cache policy: device-coherent access
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSc1));
+}
+
 // The same for the lanes of one wave: the wave's LDS operations have
 // completed, so other lanes of the wave read what it wrote.
 __device__ __forceinline__ void wave_lds_sync()
