@@ -91,21 +91,20 @@ int check_step_inputs(const tb_shape &s, const tb_step_args &a, hipStream_t st)
 }
 
 struct Ws {
-    float *scores;
     float *part_o;
     float *part_ml;
     uint32_t *counters;
     uint16_t *keys16;
+    uint16_t *keys16lo;
     uint16_t *sample16;
 };
 
 Ws carve(void *ws, const WsLayout &L)
 {
     char *base = (char *)ws;
-    return Ws{(float *)(base + L.scores),
-              (float *)(base + L.part_o), (float *)(base + L.part_ml),
+    return Ws{(float *)(base + L.part_o), (float *)(base + L.part_ml),
               (uint32_t *)(base + L.counters), (uint16_t *)(base + L.keys16),
-              (uint16_t *)(base + L.sample16)};
+              (uint16_t *)(base + L.keys16lo), (uint16_t *)(base + L.sample16)};
 }
 
 int check_ws(const tb_shape &s, void *ws, size_t ws_bytes, WsLayout *L)
@@ -199,14 +198,16 @@ int decode_step_run(const tb_shape &shape, const tb_select_params &params, const
                                             a->k_cache, a->v_cache, a->kp_cache, a->ctx_len,
                                             st)));
     if (a->refresh) {
-        // the score launch also stores the 16-bit keys and their sample,
-        // from which the selection classifies positions
-        TB_TRY(hip_rc(launch_score(shape, a->q_imp, a->kp_cache, a->ctx_len, W.scores,
+        // the score launch stores each score's key as two 16-bit halves and
+        // a sample of the top halves; the selection classifies positions
+        // from the top halves and completes only its candidates' keys
+        TB_TRY(hip_rc(launch_score(shape, a->q_imp, a->kp_cache, a->ctx_len, nullptr,
                                    fused_append ? a->n_new : 0, a->k_new, a->v_new, a->w,
-                                   a->k_cache, a->v_cache, W.keys16, W.sample16, st)));
-        TB_TRY(hip_rc(launch_select(shape, params, W.scores, a->ctx_len, a->sel_idx, stride,
+                                   a->k_cache, a->v_cache, W.keys16, W.keys16lo, W.sample16,
+                                   st)));
+        TB_TRY(hip_rc(launch_select(shape, params, nullptr, a->ctx_len, a->sel_idx, stride,
                                     a->sel_count, nullptr, a->sel_bits, a->keep_from, a->n_new,
-                                    W.keys16, W.sample16, st)));
+                                    W.keys16, W.keys16lo, W.sample16, st)));
     }
     AttnAppend app;
     if (!a->refresh && fused_append) {
@@ -348,7 +349,7 @@ int tb_score(const tb_shape *shape, const void *q_imp, const void *kp_cache,
     }
     return hip_rc(launch_score(*shape, q_imp, const_cast<void *>(kp_cache), ctx_len, scores, 0,
                                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
-                               (hipStream_t)stream));
+                               nullptr, (hipStream_t)stream));
 }
 
 int tb_select(const tb_shape *shape, const tb_select_params *params, const float *scores,
@@ -373,7 +374,7 @@ int tb_select(const tb_shape *shape, const tb_select_params *params, const float
     }
     return hip_rc(launch_select(*shape, *params, scores, ctx_len, sel_idx,
                                 sel_capacity(*shape, *params), sel_count, topb_idx, sel_bits,
-                                nullptr, 0, nullptr, nullptr, (hipStream_t)stream));
+                                nullptr, 0, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int tb_sparse_attn(const tb_shape *shape, const void *q, const void *k_cache,

@@ -196,12 +196,12 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Workspace layout (offsets in bytes from the workspace base).
 struct WsLayout {
-    size_t scores;   // fp32 scores [b][Himp][cap] (fused step only)
     size_t part_o;   // attention partial sums [b][Hq][nchunk][D] fp32
     size_t part_ml;  // attention partial (max, sum) [b][Hq][nchunk][2] fp32
     size_t counters; // attention arrival counters [b][Hkv] u32 (kept zero)
     size_t keys16;   // top 16 bits of each score's key [b][Himp][keys16_stride] u16,
                      // in pair order (fused step)
+    size_t keys16lo; // the low 16 bits, the same layout
     size_t sample16; // the same for positions 8m, compact [b][Himp][sample16_stride] u16
     size_t zeroed;       // the words that must be zero when a call starts (the
     int zeroed_words;    //  arrival counters), kept zero by every completed call
@@ -240,8 +240,6 @@ inline WsLayout ws_layout(const tb_shape &s)
 {
     WsLayout L;
     size_t off = 0;
-    L.scores = off;
-    off += align_up((size_t)s.batch * s.n_imp_heads * s.ctx_cap * sizeof(float));
     L.part_o = off;
     off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * s.head_dim *
                     sizeof(float));
@@ -252,6 +250,9 @@ inline WsLayout ws_layout(const tb_shape &s)
     L.zeroed_words = s.batch * s.n_kv_heads;
     off += align_up((size_t)s.batch * s.n_kv_heads * sizeof(uint32_t));
     L.keys16 = off;
+    off += align_up((size_t)s.batch * s.n_imp_heads * keys16_stride(s.ctx_cap) *
+                    sizeof(uint16_t));
+    L.keys16lo = off;
     off += align_up((size_t)s.batch * s.n_imp_heads * keys16_stride(s.ctx_cap) *
                     sizeof(uint16_t));
     L.sample16 = off;
@@ -290,23 +291,25 @@ hipError_t launch_append_project(const tb_shape &s, const void *k_new, const voi
 // appends the n_new rows of k_new / v_new at [ctx - n_new, ctx), projects
 // and scores them.
 int score_max_fused_new();
-// When keys16 is not NULL the launch also stores the top 16 bits of every
-// score's key into keys16[row][keys16_entry(t)] (row stride
-// keys16_stride(cap)) and, for positions t = 8m, into sample16[row][m] (row
-// stride sample16_stride(cap)).
+// When keys16 is not NULL the launch stores, instead of the fp32 scores,
+// the top and low 16 bits of every score's order-preserving key into
+// keys16 / keys16lo[row][keys16_entry(t)] (row stride keys16_stride(cap))
+// and, for positions t = 8m, the top half into sample16[row][m] (row stride
+// sample16_stride(cap)); scores is then not written.
 hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
                         const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
                         const void *v_new, const void *w, void *k_cache, void *v_cache,
-                        uint16_t *keys16, uint16_t *sample16, hipStream_t st);
+                        uint16_t *keys16, uint16_t *keys16lo, uint16_t *sample16,
+                        hipStream_t st);
 // Selection; when keep_from is not NULL it also records
-// keep_from[b] = max(0, ctx_len[b] - n_new).  keys16 / sample16 (or NULL):
-// the score launch's 16-bit keys of the same scores, which let the first
-// pass read half the bytes.
+// keep_from[b] = max(0, ctx_len[b] - n_new).  keys16 / keys16lo / sample16
+// (or NULL): the score launch's split keys, read in place of the fp32
+// scores (which may then be NULL); the first pass reads the top halves only.
 hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const float *scores,
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
                          int32_t *keep_from, int n_new, const uint16_t *keys16,
-                         const uint16_t *sample16, hipStream_t st);
+                         const uint16_t *keys16lo, const uint16_t *sample16, hipStream_t st);
 // Rows a reuse step appends inside the attention launch (bitmap mode, at
 // most score_max_fused_new() of them): the launch copies them into the
 // caches and projects their keys, and reads them from k_new / v_new.

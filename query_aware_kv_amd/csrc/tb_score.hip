@@ -15,9 +15,11 @@
 //
 // Precision contract: a score is the fp32 fused multiply-add chain over the
 // d coordinates in ascending order, starting from +0; this fp32 value is the
-// selection key.  In the fused step the top 16 bits of its order-preserving
-// key are stored as well (and compactly for positions 8m), so the selection
-// can classify positions from half the bytes.
+// selection key.  The fused step stores the two 16-bit halves of its
+// order-preserving key in two arrays instead of the fp32 value (and the top
+// half again, compactly, for positions 8m): the selection classifies
+// positions from the top halves alone and completes only its candidates'
+// keys.
 //
 // When the call also appends tokens, one extra work-group per (sequence, KV
 // head) -- the first one dispatched -- writes the new K/V rows into the
@@ -45,19 +47,24 @@ struct ScoreArgs {
     const void *w;             // [D][d]
     void *k_cache, *v_cache;
     uint16_t *keys16;   // [b][Himp][k16s] top 16 key bits of every score (pair order), or NULL
+    uint16_t *keys16lo; // [b][Himp][k16s] the low 16 key bits, the same order
     uint16_t *sample16; // [b][Himp][s16] the same for positions 8m
     int s16, k16s;
 };
 
-// Stores the score of (row, t) and, when asked, its 16-bit key.
+// Stores the score of (row, t): the fp32 value, or the two 16-bit halves of
+// its order-preserving key (and the top half again for positions 8m).
 __device__ __forceinline__ void put_score(const ScoreArgs &a, size_t row, int t, float v)
 {
-    a.scores[row * a.cap + t] = v;
     if (a.keys16 != nullptr) {
-        const uint16_t k16 = (uint16_t)(score_key(v) >> 16);
-        a.keys16[row * a.k16s + keys16_entry(t)] = k16;
+        const uint32_t key = score_key(v);
+        const size_t e = row * a.k16s + keys16_entry(t);
+        a.keys16[e] = (uint16_t)(key >> 16);
+        a.keys16lo[e] = (uint16_t)(key & 0xFFFFu);
         if ((t & 7) == 0)
-            a.sample16[row * a.s16 + (t >> 3)] = k16;
+            a.sample16[row * a.s16 + (t >> 3)] = (uint16_t)(key >> 16);
+    } else {
+        a.scores[row * a.cap + t] = v;
     }
 }
 
@@ -256,7 +263,8 @@ int score_max_fused_new() { return kMaxFusedNew; }
 hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
                         const int32_t *ctx_len, float *scores, int n_new, const void *k_new,
                         const void *v_new, const void *w, void *k_cache, void *v_cache,
-                        uint16_t *keys16, uint16_t *sample16, hipStream_t st)
+                        uint16_t *keys16, uint16_t *keys16lo, uint16_t *sample16,
+                        hipStream_t st)
 {
     ScoreArgs a;
     a.q_imp = q_imp;
@@ -275,6 +283,7 @@ hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.keys16 = keys16;
+    a.keys16lo = keys16lo;
     a.sample16 = sample16;
     a.s16 = sample16_stride(s.ctx_cap);
     a.k16s = keys16_stride(s.ctx_cap);

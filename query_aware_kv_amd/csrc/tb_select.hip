@@ -286,7 +286,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     int32_t *__restrict__ sel_count, int32_t *__restrict__ topb_idx,
     uint32_t *__restrict__ sel_bits, int bits_stride, int32_t *__restrict__ keep_from, int n_new,
     int n_sink, int n_local, const uint16_t *__restrict__ keys16,
-    const uint16_t *__restrict__ sample16, int s16)
+    const uint16_t *__restrict__ keys16lo, const uint16_t *__restrict__ sample16, int s16)
 {
     static_assert(!K16 || WPT <= 1, "16-bit first pass: one word per thread, or words re-read");
     static_assert(THREADS == 1024 || (THREADS == 512 && K16), "1024 threads, or 512 on rows of <= 512 words");
@@ -306,7 +306,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.y, i = blockIdx.x;
     const size_t rowid = (size_t)b * Himp + i;
-    const float *row = scores + rowid * cap;
+    // fp32 scores (without 16-bit keys), or the keys' two 16-bit halves
+    const float *row = K16 ? nullptr : scores + rowid * cap;
     // With 16-bit keys, this thread's four sample keys (positions 8m,
     // m = 4 tid .. 4 tid + 3) and its word's 32 keys are requested before
     // the context length is known, the sample first so that its histogram
@@ -326,6 +327,33 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             kv[q] = src[q];
+    };
+    // the full keys of word w from their two halves (pair j of a word holds
+    // positions j and 16 + j); positions outside [lo, hi) get key 0
+    auto k32_word = [&](int w, int lo_, int hi_, uint32_t (&k)[32]) {
+        const size_t base = rowid * (size_t)(32 * (wlast + 1)) + 32 * (w < wlast ? w : wlast);
+        const uint4 *ph = reinterpret_cast<const uint4 *>(keys16 + base);
+        const uint4 *pl = reinterpret_cast<const uint4 *>(keys16lo + base);
+        uint4 hv[4], lv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            hv[q] = ph[q];
+            lv[q] = pl[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t hp[4] = {hv[q].x, hv[q].y, hv[q].z, hv[q].w};
+            const uint32_t lp[4] = {lv[q].x, lv[q].y, lv[q].z, lv[q].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = 4 * q + c;
+                k[j] = (hp[c] << 16) | (lp[c] & 0xFFFFu);
+                k[16 + j] = (hp[c] & 0xFFFF0000u) | (lp[c] >> 16);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 32; ++e)
+            k[e] = 32 * w + e >= lo_ && 32 * w + e < hi_ ? k[e] : 0u;
     };
     auto s16_word = [&](int w) {
         const int ms = 4 * w < s16 ? 4 * w : s16 - 4;
@@ -374,7 +402,13 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
         load_word_keys(row, tid, lo, hi, n, vec, keys);
     // fn(w, k) over this thread's words, k[e] the key of position 32w + e
     auto for_words = [&](auto &&fn) {
-        if constexpr (REG) {
+        if constexpr (K16) {
+            for (int j = 0; j < (WPT > 0 ? 1 : nwt); ++j) {
+                uint32_t k[32];
+                k32_word(tid + j * THREADS, lo, hi, k);
+                fn(tid + j * THREADS, k);
+            }
+        } else if constexpr (REG) {
             fn(tid, keys);
         } else if constexpr (WPT > 0) {
             uint32_t k[32];
@@ -602,9 +636,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
                 __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0)
                 __builtin_amdgcn_wave_barrier();
                 const uint32_t nc = run < (uint32_t)kWaveCap ? run : (uint32_t)kWaveCap;
+                const size_t kbase = rowid * (size_t)(32 * (wlast + 1));
                 for (uint32_t e0 = 0; e0 < nc; e0 += 4 * 64) {
                     uint32_t pos[4];
-                    float f[4];
+                    uint32_t f[4];
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         // (every lane reads a slot, masked after: no branch
@@ -613,16 +648,26 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
                         const uint32_t pv = cwave[e < nc ? e : 0u].y;
                         pos[t] = pv & (0u - (uint32_t)(e < nc));
                     }
+                    uint32_t flo[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        f[t] = row[pos[t]];
+                    for (int t = 0; t < 4; ++t) {
+                        if constexpr (K16) {
+                            // the key's two halves
+                            const size_t en = kbase + keys16_entry((int)pos[t]);
+                            f[t] = keys16[en];
+                            flo[t] = keys16lo[en];
+                        } else {
+                            f[t] = __float_as_uint(row[pos[t]]);
+                        }
+                    }
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         // the key is stored by every lane (past the list
                         // into a word of its own in the prefix-list area,
                         // written only later), so no branch holds the loads
                         const uint32_t e = e0 + 64 * t + lane;
-                        const uint32_t kc = score_key(f[t]);
+                        const uint32_t kc =
+                            K16 ? (f[t] << 16) | flo[t] : score_key(__uint_as_float(f[t]));
                         *(e < nc ? &cwave[e < nc ? e : 0u].x : &tot[64 + lane]) = kc;
                         if (lvl && e < nc)
                             atomicAdd(&hist[(kc >> 12) - d0], 1u);
@@ -919,7 +964,7 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
                     const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                     int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
                     int32_t *keep_from, int n_new, const uint16_t *keys16,
-                    const uint16_t *sample16, hipStream_t st)
+                    const uint16_t *keys16lo, const uint16_t *sample16, hipStream_t st)
 {
     const int nwc = sel_words(s.ctx_cap);
     const size_t lds = sel_lds_bytes(s.ctx_cap, THREADS / 64);
@@ -945,7 +990,7 @@ hipError_t select_t(const tb_shape &s, const tb_select_params &p, const float *s
     hipLaunchKernelGGL((select_kernel<WPT, K16, THREADS>), grid, dim3(THREADS), lds, st, scores,
                        ctx_len, s.n_imp_heads, s.ctx_cap, nwc, p.budget, p.radius, sel_idx,
                        sel_stride, sel_count, topb_idx, sel_bits, bitmap_words(s.ctx_cap),
-                       keep_from, n_new, p.n_sink, p.n_local, keys16, sample16,
+                       keep_from, n_new, p.n_sink, p.n_local, keys16, keys16lo, sample16,
                        sample16_stride(s.ctx_cap));
     return hipGetLastError();
 }
@@ -956,15 +1001,15 @@ hipError_t launch_select(const tb_shape &s, const tb_select_params &p, const flo
                          const int32_t *ctx_len, int32_t *sel_idx, int sel_stride,
                          int32_t *sel_count, int32_t *topb_idx, uint32_t *sel_bits,
                          int32_t *keep_from, int n_new, const uint16_t *keys16,
-                         const uint16_t *sample16, hipStream_t st)
+                         const uint16_t *keys16lo, const uint16_t *sample16, hipStream_t st)
 {
 #define TB_SEL_ARGS                                                                          \
     s, p, scores, ctx_len, sel_idx, sel_stride, sel_count, topb_idx, sel_bits, keep_from,       \
-        n_new, keys16, sample16, st
+        n_new, keys16, keys16lo, sample16, st
     static_assert(kSelThreads == 1024, "select_key16: one word per thread up to 1024 words");
     static_assert(kSelShortCap / 32 <= 512 && kSelShortCap / 8 <= 4 * 512,
                   "short rows: one word and four sample keys per thread of 512");
-    const bool k16 = keys16 != nullptr && sample16 != nullptr;
+    const bool k16 = keys16 != nullptr && keys16lo != nullptr && sample16 != nullptr;
     if (select_key16(s.ctx_cap)) {
         if (k16) {
             if (s.ctx_cap <= kSelShortCap)
