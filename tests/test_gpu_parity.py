@@ -267,8 +267,13 @@ def _small(**kw) -> Workload:
     # rows, which the attention streams once for all of them
     dict(n_q_heads=16, n_kv_heads=2, n_imp_heads=2),
     dict(dtype="f32", head_dim=64, d_imp=16, n_imp_heads=2),
+    # rows of 513..1024 words (1024-thread selection), most of every row
+    # past the sequences' lengths
+    dict(ctx0=19999, budget=600),
+    dict(ctx0=19999, budget=600, n_sink=4, n_local=64, dtype="f32", head_dim=64, d_imp=16),
 ], ids=["base", "f32", "imp_per_kv", "group8", "B1", "dense", "r40", "mha_d64", "sink_local",
-        "buffers_cover", "sink_local_f32", "group8_shared", "f32_shared"])
+        "buffers_cover", "sink_local_f32", "group8_shared", "f32_shared", "cap20000",
+        "cap20000_f32_sink_local"])
 def test_ragged_batch_fused(kw):
     # three sequences of different lengths (1, 700 and 2000 tokens) in one launch
     w = _small(**kw)
@@ -345,8 +350,9 @@ def _rows(rng, w, n_new):
 @pytest.mark.parametrize("kw", [dict(), dict(ctx0=1996), dict(ctx0=7000, budget=300, batch=40,
                                                             n_q_heads=16, n_kv_heads=2,
                                                             n_imp_heads=4, n_sink=2,
-                                                            n_local=100)],
-                         ids=["small_grid", "odd_capacity", "windowed_grid"])
+                                                            n_local=100),
+                                dict(ctx0=20000, budget=700)],
+                         ids=["small_grid", "odd_capacity", "windowed_grid", "cap20000"])
 def test_multi_row_appends(kw, n_new):
     # steps that append several rows: up to 8 inside the first launch of the
     # step (the score launch on refresh steps, the attention launch on reuse
@@ -533,8 +539,10 @@ def test_select_single_and_empty_contexts():
 
 
 @pytest.mark.parametrize("kw", [dict(dtype="f32", head_dim=64, d_imp=16),
-                                dict(dtype="bf16", head_dim=128, d_imp=32, ctx0=5000, budget=400)],
-                         ids=["f32_radix", "bf16_sampled"])
+                                dict(dtype="bf16", head_dim=128, d_imp=32, ctx0=5000, budget=400),
+                                # rows of 513..1024 words (1024-thread selection)
+                                dict(dtype="bf16", head_dim=128, d_imp=32, ctx0=20000, budget=1500)],
+                         ids=["f32_radix", "bf16_sampled", "bf16_cap20001"])
 def test_tie_heavy_scores_through_score_kernel(kw):
     # integer-valued projected keys and importance queries: many exact score
     # ties, decided by position on both sides (rows under 64 words take the
