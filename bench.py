@@ -584,7 +584,7 @@ def main() -> int:
                          "per-workload kernel traces)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {a.gpus}); "
               "sharding is described in the design notes but not built", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
@@ -765,23 +765,23 @@ def main() -> int:
     torch.cuda.empty_cache()
     proj = projection_leg(w, 20)
 
-    configs = {w.name: {"workload": w.name, "timed_unit": "1 fused step", "unit": "steps/s",
+    per_workload = {w.name: {"workload": w.name, "timed_unit": "1 fused step", "unit": "steps/s",
                         "value": 1e3 / ms_step, "us_per_unit": ms_step * 1e3,
                         "graph_us_per_unit": ms_refresh_g * 1e3, "timing": "eager launches",
                         "algorithmic_bytes": step_bytes, "achieved": step_gbs,
                         "frac": step_gbs / PEAK_HBM_GBS}}
     if not a.no_configs:
-        configs[TINY_F32.name] = single_step_leg(TINY_F32, a.steps)
-        configs[BATCHED_8K.name] = layers_leg(BATCHED_8K, max(3, a.steps // 20))
-        configs[INTERVAL_16K.name] = interval_leg(INTERVAL_16K)
-        configs[LONG_128K.name] = single_step_leg(LONG_128K, a.steps)
+        per_workload[TINY_F32.name] = single_step_leg(TINY_F32, a.steps)
+        per_workload[BATCHED_8K.name] = layers_leg(BATCHED_8K, max(3, a.steps // 20))
+        per_workload[INTERVAL_16K.name] = interval_leg(INTERVAL_16K)
+        per_workload[LONG_128K.name] = single_step_leg(LONG_128K, a.steps)
 
     cpu = None
     if not a.no_cpu_baseline:
-        for name in list(configs):
+        for name in list(per_workload):
             log(f"bench: timing the CPU oracle on {name}")
-            configs[name]["cpu_baseline"] = cpu_baseline(BY_NAME[name], a.cpu_seconds)
-        cpu = configs[w.name]["cpu_baseline"]
+            per_workload[name]["cpu_baseline"] = cpu_baseline(BY_NAME[name], a.cpu_seconds)
+        cpu = per_workload[w.name]["cpu_baseline"]
 
     line = {
         "metric": METRIC,
@@ -824,7 +824,7 @@ def main() -> int:
         "predictor_mlp": {str(k): v for k, v in mlp.items()},
         "projection": proj,
         "offload": offload,
-        "configs": configs,
+        "configs": per_workload,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
