@@ -4,7 +4,8 @@
 // Significance: the full KV cache stays resident and each decode step reads
 // only the selected tokens; attention over them is ordinary softmax attention.
 //
-// Grid: (chunk of kAttnChunk positions, KV head, sequence).  A work-group
+// Grid: (chunk, KV head, sequence); a chunk is kAttnChunk positions, or two
+// or four times that past 64K positions (attn_chunk_len).  A work-group
 // handles one KV head and one chunk for all the query heads that share it
 // (GQA).  With bitmaps a chunk is every nchunk-th 32-position word of the
 // row, so each work-group takes an equal share of any dense region (an
@@ -454,7 +455,7 @@ constexpr int kAttnWindowPairs = 2;
 template <typename T, int D, int GQ, bool BITMAP, bool APPEND, int CH>
 hipError_t attn_launch_ch(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
-    const int nchunk = attn_chunks(s.ctx_cap);
+    const int nchunk = attn_chunks(s);
     const dim3 grid = APPEND ? dim3((nchunk + 1) * s.n_kv_heads * s.batch)
                              : dim3(nchunk, s.n_kv_heads, s.batch);
     // With two or more work-groups per compute unit the others fill the
@@ -482,7 +483,11 @@ hipError_t attn_launch_ch(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 template <typename T, int D, int GQ, bool BITMAP, bool APPEND>
 hipError_t attn_launch_t(const tb_shape &s, const AttnArgs &a, hipStream_t st)
 {
-    if (attn_chunk_len(s.ctx_cap) == 2 * kAttnChunk)
+    // (four times kAttnChunk needs at least two waves per query head)
+    if constexpr (GQ <= 4)
+        if (attn_chunk_len(s) == 4 * kAttnChunk)
+            return attn_launch_ch<T, D, GQ, BITMAP, APPEND, 4 * kAttnChunk>(s, a, st);
+    if (attn_chunk_len(s) == 2 * kAttnChunk)
         return attn_launch_ch<T, D, GQ, BITMAP, APPEND, 2 * kAttnChunk>(s, a, st);
     return attn_launch_ch<T, D, GQ, BITMAP, APPEND, kAttnChunk>(s, a, st);
 }
@@ -573,7 +578,7 @@ hipError_t launch_attn(const tb_shape &s, const void *q, const void *k_cache,
     a.kp = app.kp_cache;
     a.n_new = app.n_new > 0 ? app.n_new : 0;
     a.d_imp = s.d_imp;
-    a.nchunk = attn_chunks(s.ctx_cap);
+    a.nchunk = attn_chunks(s);
     a.batch = s.batch;
     if (s.dtype == TB_BF16) {
         if (s.head_dim == 64) return attn_gq<bf16_t, 64>(s, a, st);

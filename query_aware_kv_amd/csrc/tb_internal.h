@@ -208,10 +208,20 @@ struct WsLayout {
     size_t total;
 };
 
-// Positions per sparse attention work-group: twice kAttnChunk past 64K
-// positions, so that the last work-group of a KV head merges fewer partials.
-inline int attn_chunk_len(int cap) { return cap > 65536 ? 2 * kAttnChunk : kAttnChunk; }
-inline int attn_chunks(int cap) { return (cap + attn_chunk_len(cap) - 1) / attn_chunk_len(cap); }
+// Positions per sparse attention work-group: past 64K positions four times
+// kAttnChunk (twice with eight query heads per KV head, whose single wave
+// per head lists at most 64 words), so that the work-groups are about one
+// per compute unit and the last one of a KV head merges fewer partials.
+inline int attn_chunk_len(const tb_shape &s)
+{
+    if (s.ctx_cap <= 65536)
+        return kAttnChunk;
+    return s.n_q_heads / s.n_kv_heads <= 4 ? 4 * kAttnChunk : 2 * kAttnChunk;
+}
+inline int attn_chunks(const tb_shape &s)
+{
+    return (s.ctx_cap + attn_chunk_len(s) - 1) / attn_chunk_len(s);
+}
 inline int bitmap_words(int cap) { return (cap + 31) / 32; }
 
 inline int dense_chunks(int cap) { return (cap + kDenseChunk - 1) / kDenseChunk; }
@@ -231,9 +241,9 @@ __host__ __device__ inline int keys16_entry(int t)
 }
 // Chunk partials are laid out per kernel's own chunk count; the region fits
 // the larger of the two.
-inline int max_chunks(int cap)
+inline int max_chunks(const tb_shape &s)
 {
-    return attn_chunks(cap) > dense_chunks(cap) ? attn_chunks(cap) : dense_chunks(cap);
+    return attn_chunks(s) > dense_chunks(s.ctx_cap) ? attn_chunks(s) : dense_chunks(s.ctx_cap);
 }
 
 inline WsLayout ws_layout(const tb_shape &s)
@@ -241,10 +251,10 @@ inline WsLayout ws_layout(const tb_shape &s)
     WsLayout L;
     size_t off = 0;
     L.part_o = off;
-    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * s.head_dim *
+    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s) * s.head_dim *
                     sizeof(float));
     L.part_ml = off;
-    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s.ctx_cap) * 2 * sizeof(float));
+    off += align_up((size_t)s.batch * s.n_q_heads * max_chunks(s) * 2 * sizeof(float));
     L.counters = off;
     L.zeroed = off;
     L.zeroed_words = s.batch * s.n_kv_heads;

@@ -304,15 +304,17 @@ def test_ragged_batch_fused(kw):
     dict(batch=40, n_q_heads=16, n_kv_heads=2, n_imp_heads=4, n_sink=4, n_local=64),
     # 2 query heads per KV head, one importance head each
     dict(batch=20, n_q_heads=8, n_kv_heads=4, n_imp_heads=8),
-    # past 64K positions a work-group takes 2048 of them
+    # past 64K positions a work-group takes 4096 of them (2048 with eight
+    # query heads per KV head)
     dict(ctx0=70000, budget=2000, batch=16, n_q_heads=8, n_kv_heads=2, n_imp_heads=8),
-], ids=["group8", "group2", "long_chunks"])
+    dict(ctx0=70000, budget=2000, batch=16, n_q_heads=16, n_kv_heads=2, n_imp_heads=4),
+], ids=["group8", "group2", "long_chunks", "long_chunks_group8"])
 def test_windowed_attention_walk(kw):
     # a grid of at least two work-groups per compute unit: the bitmap
     # attention walks its rows in barrier-separated windows; ragged lengths
     # leave some chunks with no positions and others ending mid-word
     w = _small(**{"ctx0": 7000, "budget": 300, **kw})
-    chunk = 2048 if w.ctx_cap > 65536 else 1024
+    chunk = 1024 if w.ctx_cap <= 65536 else (4096 if w.group <= 4 else 2048)
     wgs = -(-w.ctx_cap // chunk) * w.n_kv_heads * w.batch
     assert wgs >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
     dc = device_case(w)
