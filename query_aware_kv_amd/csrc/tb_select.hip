@@ -400,10 +400,17 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     uint32_t keys[32];
     if constexpr (REG)
         load_word_keys(row, tid, lo, hi, n, vec, keys);
+    // With split keys and one word per thread, the word's full keys are
+    // assembled once before the radix passes, which then read them from
+    // registers, and once more for the kept words (SPLIT1: for_words reads
+    // them there).
+    constexpr bool SPLIT1 = K16 && WPT > 0;
     // fn(w, k) over this thread's words, k[e] the key of position 32w + e
     auto for_words = [&](auto &&fn) {
-        if constexpr (K16) {
-            for (int j = 0; j < (WPT > 0 ? 1 : nwt); ++j) {
+        if constexpr (SPLIT1) {
+            fn(tid, keys);
+        } else if constexpr (K16) {
+            for (int j = 0; j < nwt; ++j) {
                 uint32_t k[32];
                 k32_word(tid + j * THREADS, lo, hi, k);
                 fn(tid + j * THREADS, k);
@@ -802,6 +809,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
         }
         if (!found) {
             // ---- radix select over every key ----
+            if constexpr (SPLIT1)
+                k32_word(tid, lo, hi, keys);
             uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
             for (int pass = 0; pass < 4; ++pass) {
                 const int shift = 24 - 8 * pass;
@@ -847,6 +856,8 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
 
     // ---- kept-set bitmap (and tie bitmap when ties are split) ----
     if (!emitted) {
+        if constexpr (SPLIT1)
+            k32_word(tid, lo, hi, keys);
         for_words([&](int w, const auto &k) {
             if (w >= nw)
                 return;
