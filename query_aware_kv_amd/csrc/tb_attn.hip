@@ -39,7 +39,8 @@
 //   5. The last work-group of a (sequence, KV head) to arrive (device-scope
 //      counter) merges the chunk partials -- max and weights first, then the
 //      weighted sums with all of its threads -- writes the output rows, and
-//      resets the counter to zero for the next call.
+//      resets the counter to zero for the next call.  A row of one chunk
+//      writes its output directly.
 // Reuse steps of the fused step append their few new rows inside this
 // launch: one more work-group per (sequence, KV head), dispatched after all
 // attention work-groups, stores them in the caches and projects their keys,
@@ -437,14 +438,27 @@ __attribute__((amdgpu_waves_per_eu(WIN > 0 && !APPEND ? 8 : 1))) void attn_kerne
                 O = fmaf(mrg_acc[h2][pp][dim], f, O);
                 Ls = fmaf(mrg_l[h2][pp], f, Ls);
             }
-            publish_partial<D>(a.part_o, a.part_ml, (head0 + h2) * nchunk + c, dim, O, M, Ls);
+            if (nchunk == 1) {
+                // the only chunk: its partial is the result (what the merge
+                // of one partial computes, bit for bit)
+                const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+                reinterpret_cast<T *>(a.out)[(head0 + h2) * D + dim] = from_f32<T>(O * inv);
+            } else {
+                publish_partial<D>(a.part_o, a.part_ml, (head0 + h2) * nchunk + c, dim, O, M,
+                                   Ls);
+            }
         }
+    } else if (nchunk == 1) {
+        // an empty row: zero outputs, as the merge of no partials gives
+        for (int pi = tid; pi < GQ * D; pi += kAttnThreads)
+            reinterpret_cast<T *>(a.out)[head0 * D + pi] = from_f32<T>(0.f);
     }
 
     // ---- 5. arrival; the last work-group of this (b, g) merges the chunks ----
-    arrive_and_combine<T, D, GQ, kAttnThreads, NCH>(
-        cmb, &a.counters[(size_t)b * a.Hkv + g], a.part_o, a.part_ml, nchunk,
-        nact, head0, (T *)a.out);
+    if (nchunk > 1)
+        arrive_and_combine<T, D, GQ, kAttnThreads, NCH>(
+            cmb, &a.counters[(size_t)b * a.Hkv + g], a.part_o, a.part_ml, nchunk,
+            nact, head0, (T *)a.out);
 }
 
 // Word pairs per step of the windowed walk.

@@ -112,3 +112,40 @@ def test_dense_agrees_with_sparse_over_everything():
                     sel_bits=bits)
     torch.cuda.synchronize()
     assert float((out.float() - out2.float()).abs().max()) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(dtype="f32", head_dim=64, d_imp=16, n_q_heads=4,
+                                            n_kv_heads=4, n_imp_heads=4)],
+                         ids=["bf16_g4", "f32_mha_d64"])
+def test_sparse_one_chunk_rows(kw):
+    # a capacity of at most one attention chunk: every work-group writes its
+    # outputs directly (no partials, no arrival); an empty row gives zeros,
+    # bitmaps and lists agree, and a repeated call gives the same bits
+    w = _w(ctx0=1000, **kw)
+    lens = [0, 1, 700, 1000]
+    w = Workload(**{**w.__dict__, "batch": len(lens)})
+    pre, q, K, V, ctx, ws, _ = _run_dense(w, lens)
+    shape = shape_of(w)
+    bits = torch.full((w.batch, w.n_imp_heads, tbl.bitmap_words(shape)), -1, dtype=torch.int32,
+                      device="cuda")
+    out = torch.full((w.batch, w.n_q_heads, w.head_dim), float("nan"), dtype=K.dtype,
+                     device="cuda")
+    tbl.sparse_attn(shape, q, K, V, None, 0, None, None, ctx, w.softmax_scale, out, ws,
+                    sel_bits=bits)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[0]) == 0
+    _check(w, pre, q, out, lens)
+    out2 = torch.empty_like(out)
+    tbl.sparse_attn(shape, q, K, V, None, 0, None, None, ctx, w.softmax_scale, out2, ws,
+                    sel_bits=bits)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    # the same sets as ascending lists
+    cap_s = w.ctx_cap
+    sel = torch.arange(cap_s, dtype=torch.int32, device="cuda").expand(
+        w.batch, w.n_imp_heads, cap_s).contiguous()
+    cnt = ctx[:, None].expand(w.batch, w.n_imp_heads).contiguous()
+    out3 = torch.empty_like(out)
+    tbl.sparse_attn(shape, q, K, V, sel, cap_s, cnt, None, ctx, w.softmax_scale, out3, ws)
+    torch.cuda.synchronize()
+    assert float((out.float() - out3.float()).abs().max()) <= TOL[w.dtype]
