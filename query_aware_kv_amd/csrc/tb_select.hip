@@ -405,6 +405,24 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     // registers, and once more for the kept words (SPLIT1: for_words reads
     // them there).
     constexpr bool SPLIT1 = K16 && WPT > 0;
+    // Rows of at most THREADS / 32 words (SPLIT1): the passes over every
+    // key give each thread one key (position tid) instead of leaving a
+    // word's 32 keys to each of nw threads, whose serial LDS atomics would
+    // set the pace; the keys are staged through the candidate area, which
+    // these passes do not use otherwise.
+    const bool small = SPLIT1 && nw * 32 <= THREADS;
+    uint32_t mykey = 0u;
+    auto stage_keys = [&]() {
+        uint32_t *kst = reinterpret_cast<uint32_t *>(cpair);
+        k32_word(tid, lo, hi, keys);
+        if (tid < nw) {
+#pragma unroll
+            for (int e = 0; e < 32; ++e)
+                kst[32 * tid + e] = keys[e];
+        }
+        __syncthreads();
+        mykey = tid < 32 * nw ? kst[tid] : 0u;
+    };
     // fn(w, k) over this thread's words, k[e] the key of position 32w + e
     auto for_words = [&](auto &&fn) {
         if constexpr (SPLIT1) {
@@ -809,12 +827,21 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
         }
         if (!found) {
             // ---- radix select over every key ----
-            if constexpr (SPLIT1)
-                k32_word(tid, lo, hi, keys);
+            if constexpr (SPLIT1) {
+                if (small)
+                    stage_keys();
+                else
+                    k32_word(tid, lo, hi, keys);
+            }
             uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)B;
             for (int pass = 0; pass < 4; ++pass) {
                 const int shift = 24 - 8 * pass;
                 radix_pass(shift, prefix, krem, true, [&]() {
+                    if (small) {
+                        if (mykey != 0u && (mykey & pmask) == prefix)
+                            atomicAdd(&h16[(mykey >> shift) & 255u], 1u);
+                        return;
+                    }
                     for_words([&](int w, const auto &k) {
                         (void)w;
 #pragma unroll
@@ -855,7 +882,26 @@ __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(
     }
 
     // ---- kept-set bitmap (and tie bitmap when ties are split) ----
-    if (!emitted) {
+    if (!emitted && small) {
+        // one key per thread: a word's bits are a ballot of its 32 lanes
+        if (take_all)
+            stage_keys();
+        const bool kept = !none_kept && (thr == 0u ? mykey != 0u : (mykey & fmask) >= thr);
+        const bool tie = partial_ties && mykey != 0u && (mykey & fmask) == tau;
+        const uint64_t bk = __ballot(kept), bq = __ballot(tie);
+        if (lane == 0) {
+            const int w0 = 2 * wave;
+            if (w0 < nw) {
+                Tb[w0] = (uint32_t)bk;
+                Sb[w0] = (uint32_t)bq;
+            }
+            if (w0 + 1 < nw) {
+                Tb[w0 + 1] = (uint32_t)(bk >> 32);
+                Sb[w0 + 1] = (uint32_t)(bq >> 32);
+            }
+        }
+        __syncthreads();
+    } else if (!emitted) {
         if constexpr (SPLIT1)
             k32_word(tid, lo, hi, keys);
         for_words([&](int w, const auto &k) {
