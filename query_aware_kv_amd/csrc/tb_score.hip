@@ -21,6 +21,11 @@
 // positions from the top halves alone and completes only its candidates'
 // keys.
 //
+// Where the grid runs in several rounds of work-groups per compute unit, each
+// wave of the fused step stages its positions' split keys in LDS and writes
+// them as 16-byte pieces, one store instruction per wave instead of two
+// 2-byte ones per importance head and lane.
+//
 // When the call also appends tokens, one extra work-group per (sequence, KV
 // head) -- the first one dispatched -- writes the new K/V rows into the
 // caches, projects their keys (fp64 sum in ascending head_dim order, rounded
@@ -50,6 +55,7 @@ struct ScoreArgs {
     uint16_t *keys16lo; // [b][Himp][k16s] the low 16 key bits, the same order
     uint16_t *sample16; // [b][Himp][s16] the same for positions 8m
     int s16, k16s;
+    int wide;           // score_kernel<..., true>: split keys of whole waves through LDS
 };
 
 // Stores the score of (row, t): the fp32 value, or the two 16-bit halves of
@@ -85,13 +91,11 @@ __device__ __forceinline__ void load_queries(const ScoreArgs &a, int b, int g,
 }
 
 template <typename T, int DI, int GI>
-__device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, int t,
-                                            const float (&k)[DI], bool valid,
-                                            const uint4 (&qv)[GI][DI * sizeof(T) / 16])
+__device__ __forceinline__ void score_acc(const float (&k)[DI],
+                                          const uint4 (&qv)[GI][DI * sizeof(T) / 16],
+                                          float (&acc)[GI])
 {
     constexpr int EPC = 16 / sizeof(T);
-    const size_t row0 = (size_t)b * a.Himp + (size_t)g * GI;
-    float acc[GI];
 #pragma unroll
     for (int hh = 0; hh < GI; ++hh) {
         acc[hh] = 0.f;
@@ -104,13 +108,45 @@ __device__ __forceinline__ void score_heads(const ScoreArgs &a, int b, int g, in
                 acc[hh] = fmaf(to_f32(q[e]), k[p * EPC + e], acc[hh]);
         }
     }
-    if (valid)
-#pragma unroll
-        for (int hh = 0; hh < GI; ++hh)
-            put_score(a, row0 + hh, t, acc[hh]);
 }
 
-template <typename T, int D, int DI, int GI>
+// The split keys of a wave's 64 positions t0w .. t0w + 63, all of them below
+// the appended rows: staged in LDS in pair order, then stored as 16-byte
+// pieces -- one store instruction for the 2 * GI lines of 64 entries (128
+// bytes each) instead of 2 * GI two-byte ones per lane -- and the sample's
+// 8 entries per head as one more.  Same values and addresses as put_score.
+template <int GI>
+__device__ __forceinline__ void put_keys_wave(const ScoreArgs &a, size_t row0, int t0w, int lane,
+                                              const float (&acc)[GI],
+                                              uint16_t (&stg)[2 * GI][64])
+{
+    const int e = keys16_entry(lane); // the entry of position t0w + lane
+#pragma unroll
+    for (int hh = 0; hh < GI; ++hh) {
+        const uint32_t key = score_key(acc[hh]);
+        stg[2 * hh][e] = (uint16_t)(key >> 16);
+        stg[2 * hh + 1][e] = (uint16_t)(key & 0xFFFFu);
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int idx = lane; idx < 16 * GI; idx += 64) {
+        const int line = idx >> 3, q = idx & 7;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&stg[line][8 * q]);
+        uint16_t *arr = (line & 1) ? a.keys16lo : a.keys16;
+        *reinterpret_cast<uint4 *>(arr + (row0 + (line >> 1)) * a.k16s + t0w + 8 * q) = v;
+    }
+    if (lane < GI) {
+        uint32_t s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            s[i] = (uint32_t)stg[2 * lane][keys16_entry(16 * i)] |
+                   ((uint32_t)stg[2 * lane][keys16_entry(16 * i + 8)] << 16);
+        *reinterpret_cast<uint4 *>(a.sample16 + (row0 + lane) * a.s16 + (t0w >> 3)) =
+            make_uint4(s[0], s[1], s[2], s[3]);
+    }
+}
+
+template <typename T, int D, int DI, int GI, bool WIDE>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
 {
     // 1-D grid.  With appended rows the first batch*Hkv work-groups (the
@@ -222,7 +258,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a)
                 k[p * EPC + e] = to_f32(v[e]);
         }
     }
-    score_heads<T, DI, GI>(a, b, g, t, k, valid, qv);
+    float acc[GI];
+    score_acc<T, DI, GI>(k, qv, acc);
+    const size_t row0 = (size_t)b * a.Himp + (size_t)g * GI;
+    if constexpr (WIDE) {
+        const int lane = threadIdx.x & 63;
+        const int t0w = t - lane; // the wave's first position
+        __shared__ __align__(16) uint16_t stg[kScoreThreads / 64][2 * GI][64];
+        if (t0w + 64 <= t_new) {
+            put_keys_wave<GI>(a, row0, t0w, lane, acc, stg[threadIdx.x >> 6]);
+            return;
+        }
+    }
+    if (valid) {
+#pragma unroll
+        for (int hh = 0; hh < GI; ++hh)
+            put_score(a, row0 + hh, t, acc[hh]);
+    }
 }
 
 template <typename T, int D, int DI, int GI>
@@ -230,7 +282,10 @@ hipError_t score_t(const tb_shape &s, const ScoreArgs &a, hipStream_t st)
 {
     const int bg = s.batch * s.n_kv_heads;
     dim3 grid((a.n_new > 0 ? bg : 0) + a.ntiles * bg);
-    hipLaunchKernelGGL((score_kernel<T, D, DI, GI>), grid, dim3(kScoreThreads), 0, st, a);
+    if (a.wide)
+        hipLaunchKernelGGL((score_kernel<T, D, DI, GI, true>), grid, dim3(kScoreThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((score_kernel<T, D, DI, GI, false>), grid, dim3(kScoreThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -287,6 +342,16 @@ hipError_t launch_score(const tb_shape &s, const void *q_imp, void *kp_cache,
     a.sample16 = sample16;
     a.s16 = sample16_stride(s.ctx_cap);
     a.k16s = keys16_stride(s.ctx_cap);
+    // The 16-byte key stores pay where the grid runs in several rounds of
+    // work-groups per compute unit (a round's writes then overlap the next
+    // round's loads: 128K context 74.3 -> 72.4 us per step); a grid of one
+    // round (32K context, 512 tiles) drains its writes at the end either
+    // way, and the staging only adds to it (32.2 -> 32.4 us).
+    int cus = 0;
+    const hipError_t ce = device_cus(cus);
+    if (ce != hipSuccess)
+        return ce;
+    a.wide = keys16 != nullptr && (long)a.ntiles * s.batch * s.n_kv_heads > 2L * cus;
     if (s.dtype == TB_BF16)
         return score_dtype<bf16_t>(s, a, st);
     return score_dtype<float>(s, a, st);
